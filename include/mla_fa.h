@@ -1,0 +1,160 @@
+/*
+ * mla_fa.h -- C ABI of the MI355X (gfx950) MLA flash-attention library.
+ *
+ * The operation: flash attention for DeepSeek-style multi-head latent attention over
+ * the compressed latent cache.  Each cache row holds kv_lora_rank 512 latent values
+ * followed by 64 RoPE values (576 in all); with flash attention the cache is K-only
+ * and V is the first 512 columns of the same row, shared by every query head
+ * ("ik_llama.cpp -mla flag deep-dive", sections "what MLA is" and "the four -mla
+ * levels").  Scores are formed tile by tile with an online softmax (running max m,
+ * running sum l, earlier terms corrected whenever m grows), so no score matrix is
+ * ever written to memory ("Vulkan backend fused Flash Attention: DeepSeek MLA local
+ * inference", sections 2.1-2.2).  The optional mask is f16 and additive after
+ * scaling; a cell whose mask is -inf is not kept ("baguaai Flash Attention tag page",
+ * f16 FA mask digest).  Sparse decoding first compacts each mask row to the ascending
+ * list of kept cells with one scan over per-segment ballot counts, then attends only
+ * to those rows ("llama.cpp Vulkan backend adds sparse Flash Attention for quantized
+ * K/V", commit text).
+ *
+ * For a query row q (576 values), keys k_j (576 values) and mask b_j:
+ *     s_j   = scale * <q, k_j> + b_j           (s_j = -inf when b_j = -inf or j is
+ *                                               past the causal edge)
+ *     out   = sum_j softmax(s)_j * k_j[0:512]   (all zeros when no key is kept)
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no memory on any of these paths and keeps no pointer after return.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; outputs are valid once the stream reaches that point.
+ *   - Arguments are validated on the host before any HIP call.  The return value is
+ *     MLA_FA_OK or a negative mla_fa_status; on error nothing was enqueued except
+ *     for MLA_FA_ERR_HIP, which reports a failed launch.  No exceptions, no abort,
+ *     no host synchronisation.  Calls are reentrant; calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Element types: q is f16 or bf16 (bits, [..][n_head][576] contiguous); the
+ *     cache is f16, bf16 or Q8_0.  Supported pairs: f16/f16, bf16/bf16, f16/Q8_0,
+ *     bf16/Q8_0.  A Q8_0 row is 18 blocks of {f16 scale d, 32 int8 codes} = 612
+ *     bytes; value = code * d.  Q8_0 is computed in f16 on the GPU, f16 caches in
+ *     f16 and bf16 caches in bf16, all with fp32 accumulation.
+ *   - n_head is a multiple of 16 in [16, 128].
+ *   - Outputs are fp32 [..][n_head][512].
+ */
+#ifndef MLA_FA_H
+#define MLA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mla_fa_type { MLA_FA_F16 = 1, MLA_FA_BF16 = 2, MLA_FA_Q8_0 = 3 };
+
+enum mla_fa_status {
+    MLA_FA_OK = 0,
+    MLA_FA_ERR_INVALID = -1,      /* null pointer, bad size, stride or alignment     */
+    MLA_FA_ERR_UNSUPPORTED = -2,  /* type pair or head count this build does not do   */
+    MLA_FA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required       */
+    MLA_FA_ERR_HIP = -4           /* a HIP launch failed                              */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *mla_fa_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mla_fa_version(void);
+
+/*
+ * Number of KV splits the library picks when a call passes n_split = 0, for a call
+ * with n_rows = n_seq * n_tok query rows.  Split-KV: each split attends to one range
+ * of keys and leaves a partial (m, l, O); the partials are merged with the same
+ * rescale-by-new-max rule the online softmax applies between tiles.
+ */
+int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type);
+
+/*
+ * Workspace bytes a call with these sizes needs (0 when n_split resolves to 1).
+ * n_split = 0 means the automatic choice.  The workspace holds the split partials
+ * (fp32 m, l and unnormalised O per split, row and head) and is fully rewritten by
+ * every call; it needs no initialisation.
+ */
+size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split);
+
+/*
+ * Decode: n_seq sequences, one query token each.
+ *   q              [n_seq][n_head][576] f16/bf16 bits (16-byte aligned).
+ *   kv             row j of sequence s at kv + s*kv_seq_stride + j*kv_row_stride
+ *                  (bytes).  f16/bf16: 16-byte aligned base and strides; Q8_0:
+ *                  4-byte aligned.  kv_seq_stride may be 0 (shared cache).
+ *   n_kv           rows per sequence, 1 .. 2^31-1.
+ *   mask           NULL, or f16 bits [n_seq][mask_seq_stride] (elements); element
+ *                  (s, j) is added to score j of every head of sequence s.
+ *   kv_idx         NULL for dense decoding.  Otherwise the sparse path: per
+ *   kv_idx_count   sequence s, kv_idx[s*idx_seq_stride + c] for c < kv_idx_count[s]
+ *   idx_seq_stride is an ascending list of cache rows to attend to (as written by
+ *                  fa_mask_compact); both arrays live on the device, the count is
+ *                  read by the kernels, so there is no host synchronisation.  The
+ *                  mask, if given, is still added at the gathered rows.
+ *   scale          finite fp32 softmax scale (e.g. 1/sqrt(192)).
+ *   out            [n_seq][n_head][512] fp32.
+ *   n_split        0 = automatic, else 1 .. 1024 KV splits.
+ *   workspace      device buffer of at least mla_fa_workspace_size(n_seq, n_head,
+ *                  n_kv, kv_type, n_split) bytes (may be NULL when that is 0).
+ */
+int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                  int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv,
+                  const uint16_t *mask, int64_t mask_seq_stride, const int32_t *kv_idx,
+                  const int32_t *kv_idx_count, int64_t idx_seq_stride, float scale, float *out,
+                  int n_split, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two phases of mla_fa_decode, for callers that time or overlap them.
+ * mla_fa_decode_partials runs the split attention and, for n_split > 1, leaves the
+ * partials in the workspace (for n_split == 1 it writes `out` directly and there is
+ * nothing to merge).  mla_fa_merge_partials combines the partials of a previous
+ * mla_fa_decode_partials call with the same n_rows (= n_seq), n_head, n_split and
+ * workspace into `out`.  mla_fa_decode is exactly these two calls in order.
+ */
+int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_type,
+                           int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq, int n_head,
+                           int64_t n_kv, const uint16_t *mask, int64_t mask_seq_stride,
+                           const int32_t *kv_idx, const int32_t *kv_idx_count,
+                           int64_t idx_seq_stride, float scale, float *out, int n_split,
+                           void *workspace, size_t workspace_bytes, void *stream);
+int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
+ * Chunked prefill: n_tok query tokens of one sequence against its cache of n_kv rows
+ * (the chunk's tokens are the last n_tok positions of the cache).
+ *   q        [n_tok][n_head][576] f16/bf16 bits.
+ *   kv       row j at kv + j*kv_row_stride (bytes), alignment as for decode.
+ *   causal   nonzero: token t attends to keys j <= n_kv - n_tok + t; requires
+ *            n_tok <= n_kv.
+ *   mask     NULL, or f16 bits [n_tok][mask_row_stride], added per (token, key).
+ *   out      [n_tok][n_head][512] fp32.
+ *   n_split / workspace as for decode (with n_rows = n_tok).
+ */
+int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                   int n_tok, int n_head, int64_t n_kv, int causal, const uint16_t *mask,
+                   int64_t mask_row_stride, float scale, float *out, int n_split,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Sparse-mask index compaction.  For each of n_rows f16 mask rows (row r at
+ * mask + r*mask_row_stride elements, n_kv cells), writes the ascending list of cells
+ * whose mask is not -inf (bit pattern != 0xFC00) to idx + r*idx_row_stride and its
+ * length to count[r].  Entries of idx past count[r] are left untouched.  One
+ * workgroup per row: each wavefront owns one contiguous segment of the row, counts
+ * its kept cells with ballots over coalesced loads, one exclusive scan over the
+ * segment counts gives every segment its output offset, then each wavefront writes
+ * its cells.  idx_row_stride >= n_kv; n_kv <= 2^31-1.
+ */
+int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                    int32_t *idx, int64_t idx_row_stride, int32_t *count, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_FA_H */

@@ -1,0 +1,317 @@
+// api.hip -- the extern "C" boundary of libmlafa: argument validation (before any HIP
+// call), split planning, workspace layout and launches.  See include/mla_fa.h for the
+// contract of every entry point.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mla_fa.h"
+#include "mla_fa_internal.h"
+
+using namespace mlafa;
+
+namespace {
+
+constexpr int kCUs = 256;                    // MI355X compute units (one workgroup each)
+constexpr int kMinTilesPerSplit = 2;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int kv_kind_of(int kv_type) {
+    return kv_type == MLA_FA_BF16 ? KV_BF16 : kv_type == MLA_FA_F16 ? KV_F16 : KV_Q8;
+}
+
+int check_types(int q_type, int kv_type) {
+    if (q_type != MLA_FA_F16 && q_type != MLA_FA_BF16) return MLA_FA_ERR_INVALID;
+    if (kv_type != MLA_FA_F16 && kv_type != MLA_FA_BF16 && kv_type != MLA_FA_Q8_0)
+        return MLA_FA_ERR_INVALID;
+    if (kv_type == MLA_FA_Q8_0) return MLA_FA_OK;
+    if (kv_type != q_type) return MLA_FA_ERR_UNSUPPORTED;
+    return MLA_FA_OK;
+}
+
+int check_heads(int n_head) {
+    if (n_head < 1) return MLA_FA_ERR_INVALID;
+    if (n_head % 16 != 0 || n_head > 128) return MLA_FA_ERR_UNSUPPORTED;
+    return MLA_FA_OK;
+}
+
+int row_bytes(int kv_type) { return kv_type == MLA_FA_Q8_0 ? kQ8RowBytes : kRowBytes16; }
+
+// Environment override of the automatic split count (tuning only; results change by
+// float reassociation alone).
+int env_splits() {
+    const char *e = std::getenv("MLA_FA_NSPLIT");
+    if (!e || !*e) return 0;
+    int v = std::atoi(e);
+    return v >= 1 && v <= kMaxSplits ? v : 0;
+}
+
+// Workgroup shape: heads per workgroup.  Split calls use 64-head workgroups whose two
+// key halves merge in LDS (half the partial bytes of 128-head workgroups); unsplit
+// calls use 128-head workgroups so each tile is read once per query row.
+int pick_shape(int n_head, int n_split) {
+    if (n_head <= 16) return SHAPE_H16;
+    if (n_head <= 32) return SHAPE_H32;
+    if (n_head <= 64 || n_split > 1) return SHAPE_H64;
+    return SHAPE_H128;
+}
+
+int auto_splits(int64_t n_rows, int n_head, int64_t n_kv) {
+    const int env = env_splits();
+    if (env) return env;
+    const int hg_split = (n_head + shape_heads(pick_shape(n_head, 2)) - 1) / shape_heads(pick_shape(n_head, 2));
+    if (n_rows * ((n_head + shape_heads(pick_shape(n_head, 1)) - 1) / shape_heads(pick_shape(n_head, 1))) >= kCUs)
+        return 1;
+    int64_t s = (kCUs + n_rows * hg_split - 1) / (n_rows * hg_split);
+    const int64_t max_by_len = (n_kv + kTileKeys * kMinTilesPerSplit - 1) / (kTileKeys * kMinTilesPerSplit);
+    if (s > max_by_len) s = max_by_len;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return (int)s;
+}
+
+struct Plan {
+    int n_split;
+    int shape;
+    int head_groups;
+    int grid_x;
+    int64_t split_chunk;
+};
+
+Plan make_plan(int64_t n_rows, int n_head, int64_t n_kv, int n_split) {
+    Plan p;
+    p.n_split = n_split > 0 ? n_split : auto_splits(n_rows, n_head, n_kv);
+    p.shape = pick_shape(n_head, p.n_split);
+    const int hpw = shape_heads(p.shape);
+    p.head_groups = (n_head + hpw - 1) / hpw;
+    p.grid_x = p.head_groups > 1 ? 8 * p.head_groups * ((p.n_split + 7) / 8) : p.n_split;
+    int64_t chunk = (n_kv + p.n_split - 1) / p.n_split;
+    p.split_chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+    return p;
+}
+
+struct Common {
+    const void *q;
+    int q_type;
+    const void *kv;
+    int kv_type;
+    int64_t kv_row_stride, kv_seq_stride;
+    int n_seq, n_tok, n_head;
+    int64_t n_kv;
+    int causal;
+    const uint16_t *mask;
+    int64_t mask_seq_stride, mask_tok_stride;
+    const int32_t *kv_idx, *kv_idx_count;
+    int64_t idx_seq_stride;
+    float scale;
+    float *out;
+    int n_split;
+    void *ws;
+    size_t ws_bytes;
+};
+
+int validate(const Common &c) {
+    if (!c.q || !c.kv || !c.out) return MLA_FA_ERR_INVALID;
+    int st = check_types(c.q_type, c.kv_type);
+    if (st) return st;
+    st = check_heads(c.n_head);
+    if (st) return st;
+    if (c.n_seq < 1 || c.n_tok < 1 || c.n_kv < 1 || c.n_kv > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
+    if ((int64_t)c.n_seq * c.n_tok > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
+    if (!std::isfinite(c.scale)) return MLA_FA_ERR_INVALID;
+    if (c.n_split < 0 || c.n_split > kMaxSplits) return MLA_FA_ERR_INVALID;
+    if (!aligned(c.q, 16) || !aligned(c.out, 16)) return MLA_FA_ERR_INVALID;
+    const size_t kva = c.kv_type == MLA_FA_Q8_0 ? 4 : 16;
+    if (!aligned(c.kv, kva) || c.kv_row_stride < row_bytes(c.kv_type) || c.kv_row_stride % kva ||
+        c.kv_seq_stride < 0 || c.kv_seq_stride % kva)
+        return MLA_FA_ERR_INVALID;
+    if (c.causal && c.n_tok > c.n_kv) return MLA_FA_ERR_INVALID;
+    if (c.mask) {
+        if (!aligned(c.mask, 2) || c.mask_seq_stride < 0 || c.mask_tok_stride < 0)
+            return MLA_FA_ERR_INVALID;
+        if (c.n_seq > 1 && c.mask_seq_stride < c.n_kv) return MLA_FA_ERR_INVALID;
+        if (c.n_tok > 1 && c.mask_tok_stride < c.n_kv) return MLA_FA_ERR_INVALID;
+    }
+    if ((c.kv_idx == nullptr) != (c.kv_idx_count == nullptr)) return MLA_FA_ERR_INVALID;
+    if (c.kv_idx) {
+        if (c.n_tok != 1 || c.causal) return MLA_FA_ERR_INVALID;
+        if (!aligned(c.kv_idx, 4) || !aligned(c.kv_idx_count, 4)) return MLA_FA_ERR_INVALID;
+        if (c.idx_seq_stride < 1 || (c.n_seq > 1 && c.idx_seq_stride < c.n_kv)) return MLA_FA_ERR_INVALID;
+    }
+    return MLA_FA_OK;
+}
+
+int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
+    const int64_t n_rows = (int64_t)c.n_seq * c.n_tok;
+    if (p.n_split > 1) {
+        const size_t need = partial_bytes(n_rows, c.n_head, p.n_split);
+        if (!c.ws || c.ws_bytes < need || !aligned(c.ws, 16)) return MLA_FA_ERR_WORKSPACE;
+    }
+    if (n_rows > 0x7FFFFFFFLL || p.grid_x > 0x7FFFFFFF) return MLA_FA_ERR_INVALID;
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const uint16_t *>(c.q);
+    a.kv = static_cast<const uint8_t *>(c.kv);
+    a.kv_row_stride = c.kv_row_stride;
+    a.kv_seq_stride = c.kv_seq_stride;
+    a.mask = c.mask;
+    a.mask_seq_stride = c.mask_seq_stride;
+    a.mask_tok_stride = c.mask_tok_stride;
+    a.kv_idx = c.kv_idx;
+    a.kv_idx_count = c.kv_idx_count;
+    a.idx_seq_stride = c.idx_seq_stride;
+    a.out = c.out;
+    a.ws = static_cast<float *>(c.ws);
+    a.n_kv = c.n_kv;
+    a.split_chunk = p.split_chunk;
+    a.n_seq = c.n_seq;
+    a.n_tok = c.n_tok;
+    a.n_head = c.n_head;
+    a.causal = c.causal ? 1 : 0;
+    a.n_split = p.n_split;
+    a.head_groups = p.head_groups;
+    a.grid_x = p.grid_x;
+    a.q_bf16 = c.q_type == MLA_FA_BF16;
+    a.scale_log2 = c.scale * 1.4426950408889634f;
+    if (std::getenv("MLA_FA_LOG"))
+        fprintf(stderr, "mla_fa: rows=%lld heads=%d n_kv=%lld split=%d chunk=%lld shape=%d hg=%d grid=%dx%lld\n",
+                (long long)n_rows, c.n_head, (long long)c.n_kv, p.n_split, (long long)p.split_chunk,
+                p.shape, p.head_groups, p.grid_x, (long long)n_rows);
+    hipError_t e = launch_attention(a, kv_kind_of(c.kv_type), p.shape, stream);
+    return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
+int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *ws, size_t ws_bytes,
+              hipStream_t stream) {
+    if (n_split <= 1) return MLA_FA_OK;
+    const size_t need = partial_bytes(n_rows, n_head, n_split);
+    if (!ws || ws_bytes < need || !aligned(ws, 16)) return MLA_FA_ERR_WORKSPACE;
+    hipError_t e = launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws), out, stream);
+    return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
+Common decode_common(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                     int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv,
+                     const uint16_t *mask, int64_t mask_seq_stride, const int32_t *kv_idx,
+                     const int32_t *kv_idx_count, int64_t idx_seq_stride, float scale, float *out,
+                     int n_split, void *ws, size_t ws_bytes) {
+    Common c;
+    c.q = q; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
+    c.kv_row_stride = kv_row_stride; c.kv_seq_stride = kv_seq_stride;
+    c.n_seq = n_seq; c.n_tok = 1; c.n_head = n_head; c.n_kv = n_kv; c.causal = 0;
+    c.mask = mask; c.mask_seq_stride = mask_seq_stride; c.mask_tok_stride = 0;
+    c.kv_idx = kv_idx; c.kv_idx_count = kv_idx_count; c.idx_seq_stride = idx_seq_stride;
+    c.scale = scale; c.out = out; c.n_split = n_split; c.ws = ws; c.ws_bytes = ws_bytes;
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_fa_strerror(int status) {
+    switch (status) {
+        case MLA_FA_OK: return "ok";
+        case MLA_FA_ERR_INVALID: return "invalid argument (null pointer, size, stride or alignment)";
+        case MLA_FA_ERR_UNSUPPORTED: return "unsupported type pair or head count";
+        case MLA_FA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MLA_FA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int mla_fa_version(void) { return 10000; }
+
+int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type) {
+    (void)kv_type;
+    if (n_rows < 1 || n_kv < 1 || check_heads(n_head)) return 1;
+    return auto_splits(n_rows, n_head, n_kv);
+}
+
+size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split) {
+    (void)kv_type;
+    if (n_rows < 1 || n_kv < 1 || check_heads(n_head) || n_split < 0 || n_split > kMaxSplits) return 0;
+    Plan p = make_plan(n_rows, n_head, n_kv, n_split);
+    return p.n_split > 1 ? partial_bytes(n_rows, n_head, p.n_split) : 0;
+}
+
+int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_type,
+                           int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq, int n_head,
+                           int64_t n_kv, const uint16_t *mask, int64_t mask_seq_stride,
+                           const int32_t *kv_idx, const int32_t *kv_idx_count,
+                           int64_t idx_seq_stride, float scale, float *out, int n_split,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
+                             mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
+                             n_split, workspace, workspace_bytes);
+    int st = validate(c);
+    if (st) return st;
+    Plan p = make_plan(n_seq, n_head, n_kv, n_split);
+    return run_partials(c, p, static_cast<hipStream_t>(stream));
+}
+
+int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (!out || n_rows < 1 || n_split < 1 || n_split > kMaxSplits || !aligned(out, 16))
+        return MLA_FA_ERR_INVALID;
+    int st = check_heads(n_head);
+    if (st) return st;
+    return run_merge(n_rows, n_head, n_split, out, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                  int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv,
+                  const uint16_t *mask, int64_t mask_seq_stride, const int32_t *kv_idx,
+                  const int32_t *kv_idx_count, int64_t idx_seq_stride, float scale, float *out,
+                  int n_split, void *workspace, size_t workspace_bytes, void *stream) {
+    Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
+                             mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
+                             n_split, workspace, workspace_bytes);
+    int st = validate(c);
+    if (st) return st;
+    Plan p = make_plan(n_seq, n_head, n_kv, n_split);
+    if (p.n_split > 1 && (!workspace || workspace_bytes < partial_bytes(n_seq, n_head, p.n_split)))
+        return MLA_FA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_partials(c, p, s);
+    if (st) return st;
+    return run_merge(n_seq, n_head, p.n_split, out, workspace, workspace_bytes, s);
+}
+
+int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                   int n_tok, int n_head, int64_t n_kv, int causal, const uint16_t *mask,
+                   int64_t mask_row_stride, float scale, float *out, int n_split,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    Common c;
+    c.q = q; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
+    c.kv_row_stride = kv_row_stride; c.kv_seq_stride = 0;
+    c.n_seq = 1; c.n_tok = n_tok; c.n_head = n_head; c.n_kv = n_kv; c.causal = causal;
+    c.mask = mask; c.mask_seq_stride = 0; c.mask_tok_stride = mask_row_stride;
+    c.kv_idx = nullptr; c.kv_idx_count = nullptr; c.idx_seq_stride = 0;
+    c.scale = scale; c.out = out; c.n_split = n_split; c.ws = workspace; c.ws_bytes = workspace_bytes;
+    int st = validate(c);
+    if (st) return st;
+    Plan p = make_plan(n_tok, n_head, n_kv, n_split);
+    if (p.n_split > 1 && (!workspace || workspace_bytes < partial_bytes(n_tok, n_head, p.n_split)))
+        return MLA_FA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_partials(c, p, s);
+    if (st) return st;
+    return run_merge(n_tok, n_head, p.n_split, out, workspace, workspace_bytes, s);
+}
+
+int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                    int32_t *idx, int64_t idx_row_stride, int32_t *count, void *stream) {
+    if (!mask || !idx || !count || n_rows < 1 || n_kv < 1 || n_kv > 0x7FFFFFFFLL)
+        return MLA_FA_ERR_INVALID;
+    if (!aligned(mask, 2) || !aligned(idx, 4) || !aligned(count, 4)) return MLA_FA_ERR_INVALID;
+    if (idx_row_stride < n_kv || (n_rows > 1 && mask_row_stride < n_kv) || mask_row_stride < 0)
+        return MLA_FA_ERR_INVALID;
+    hipError_t e = launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
+                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
+}  // extern "C"

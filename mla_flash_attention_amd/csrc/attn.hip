@@ -1,0 +1,642 @@
+// attn.hip -- fused MLA flash attention over the latent cache for gfx950 (CDNA4).
+//
+// One kernel family serves dense decode, split-KV decode, sparse (indexed) decode and
+// causal chunked prefill.  What it computes follows the pages:
+//   * scores are built key-tile by key-tile with an online softmax: a running max m
+//     and running sum l per query head; when a tile raises m, everything accumulated
+//     before is corrected by exp(m_old - m_new) ("Vulkan backend fused Flash
+//     Attention: DeepSeek MLA local inference", sections 2.1-2.2);
+//   * the cache row is 512 latent + 64 RoPE values; V is the first 512 columns of the
+//     same row and one latent head serves every query head ("ik_llama.cpp -mla flag
+//     deep-dive", sections "what MLA is" and "the four -mla levels");
+//   * the f16 mask is additive and -inf drops a cell ("baguaai Flash Attention tag
+//     page", f16 mask digest); the sparse path attends only to the compacted rows
+//     ("llama.cpp Vulkan backend adds sparse Flash Attention for quantized K/V");
+//   * `-ctk q8_0` caches are dequantised in the kernel ("ik_llama.cpp -mla flag
+//     deep-dive", recommended command combinations).
+//
+// Design (gfx950-specific, not from the pages):
+//   * 64-key tiles of 576-wide rows are copied HBM -> LDS with global_load_lds_dwordx4
+//     (no VGPR staging), double-buffered, 16-byte chunks XOR-swizzled per row so both
+//     LDS read patterns below are bank-conflict free.  Q8_0 tiles are DMA'd raw and
+//     dequantised LDS -> LDS to f16.
+//   * Q.K^T runs as S^T = K.Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys from
+//     LDS, B = 16 heads of Q held in VGPRs for the whole kernel.  The accumulator
+//     layout (lane = head, 4 keys per lane) is exactly the A-operand layout P.V needs
+//     with heads as M, so P never round-trips through LDS.
+//   * P.V takes its B operand straight from the row-major tile with
+//     ds_read_b64_tr_b16 (LDS transpose read), so no transposed copy of V exists.
+//   * Lazy rescale: m only moves when a tile's max exceeds it by more than 2^8, so
+//     the 512-wide O accumulators are rarely touched by the softmax.
+//   * A workgroup is NW waves = (NW/WK) head sets x WK key halves; key halves merge
+//     their (m, l, O) through LDS at the end, which halves split-KV partial traffic.
+#include "mla_fa_internal.h"
+
+namespace mlafa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef unsigned u32x4 __attribute__((__vector_size__(16)));
+typedef unsigned u32x2 __attribute__((__vector_size__(8)));
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T *
+
+constexpr int kSub = 32;                                  // keys per compute sub-tile
+constexpr int kTileBytes = kTileKeys * kRowBytes16;       // 73,728
+constexpr int kChunksPerRow = kRowBytes16 / 16;           // 72
+constexpr int kDmaPerTile = kTileBytes / 1024;            // 72 wave-wide 1 KB copies
+constexpr int kQ8TileBytes = kTileKeys * kQ8RowBytes;     // 39,168
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThresh = 8.0f;                    // log2 units
+
+// Row r's 16-byte chunk c lives at chunk (c ^ swz(r)) of that row.  swz permutes the
+// low three chunk bits so that (a) 8 consecutive rows at one chunk and (b) 4
+// consecutive rows at two adjacent chunks fall into distinct LDS banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <typename T> __device__ __forceinline__ T bitcast_to(u32x4 v) {
+    return __builtin_bit_cast(T, v);
+}
+
+template <int KIND>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (KIND == KV_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast_to<bf16x8>(a), bitcast_to<bf16x8>(b),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast_to<f16x8>(a), bitcast_to<f16x8>(b),
+                                                      c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ unsigned f32_to_bf16_bits(float x) {   // nearest even
+    return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
+}
+
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (unsigned)__builtin_bit_cast(unsigned short, a) |
+           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(unsigned short b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+template <int KIND> __device__ __forceinline__ unsigned pack_p(float lo, float hi) {
+    if constexpr (KIND == KV_BF16)
+        return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    else
+        return pack_f16x2(lo, hi);
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+    // max over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+    auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+    auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+__device__ __forceinline__ int shfl_int(int v, int src_lane) {
+    return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+__device__ __forceinline__ float shfl_f(float v, int src_lane) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70 & ~0xC00F); }
+
+// ---------------------------------------------------------------------------------
+// The attention kernel.  NW waves, each owning MB blocks of 16 heads; WK waves share
+// one head set and split every 64-key tile between them (WK = 2: keys 0..31 /
+// 32..63).  Heads per workgroup = NW / WK * 16 * MB.  IDX: sparse path (rows gathered
+// through the index list).  At MB = 2 a wave holds Q (144 VGPRs) and O (256) for 32
+// heads, so the kernel runs one wave per SIMD.
+template <int MB, int NW, int WK, int KIND, bool IDX>
+__global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
+    constexpr int kHS = NW / WK;                     // head sets per workgroup
+    constexpr int kHPW = kHS * 16 * MB;              // heads per workgroup
+    constexpr bool kQ8 = KIND == KV_Q8;
+    constexpr int kStageBytes = kTileBytes;
+    constexpr int kF16Stages = kQ8 ? 1 : 2;
+    constexpr int kLdsBytes = kF16Stages * kStageBytes + (kQ8 ? 2 * kQ8TileBytes : 0);
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(kDmaPerTile % NW == 0, "tile copies split evenly over waves");
+    static_assert(WK == 1 || kHS * MB * (32 * 4 * 64 + 32) * 4 <= kLdsBytes, "key-half merge fits in LDS");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hs = wave / WK;                         // head block of this wave
+    const int kp = wave % WK;                         // key half of this wave
+    const int g = lane >> 4;                          // 16-lane group
+    const int l16 = lane & 15;
+
+    // ---- which (row, split, head group) this workgroup owns
+    int hg, split;
+    if (a.head_groups > 1) {
+        // workgroups x and x+8 are dispatched to the same XCD (round-robin over 8);
+        // give them one key range and different head groups so they share its L2.
+        const int x = blockIdx.x;
+        hg = (x >> 3) % a.head_groups;
+        split = (x & 7) + 8 * (x / (8 * a.head_groups));
+    } else {
+        hg = 0;
+        split = blockIdx.x;
+    }
+    if (split >= a.n_split) return;
+    const int n_rows = a.n_seq * a.n_tok;
+    const int row_lin = (int)blockIdx.y;
+    const int s_idx = row_lin / a.n_tok;
+    const int t_idx = a.n_tok - 1 - row_lin % a.n_tok;   // longest causal rows first
+    const int row = s_idx * a.n_tok + t_idx;
+    const uint8_t *kvs = a.kv + (int64_t)s_idx * a.kv_seq_stride;
+    const uint16_t *mrow = a.mask ? a.mask + (int64_t)s_idx * a.mask_seq_stride +
+                                        (int64_t)t_idx * a.mask_tok_stride
+                                  : nullptr;
+    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride : nullptr;
+    int64_t kend, chunk = a.split_chunk;
+    if constexpr (IDX) {
+        const int64_t c = a.kv_idx_count[s_idx];
+        kend = c < 0 ? 0 : (c > a.n_kv ? a.n_kv : c);
+        chunk = (kend + a.n_split - 1) / a.n_split;
+        chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+        if (chunk == 0) chunk = kTileKeys;
+    } else {
+        kend = a.causal ? a.n_kv - a.n_tok + t_idx + 1 : a.n_kv;
+    }
+    const int64_t k0 = (int64_t)split * chunk;
+    const int64_t k1 = k0 + chunk < kend ? k0 + chunk : kend;
+    const int n_tiles = k1 > k0 ? (int)((k1 - k0 + kTileKeys - 1) / kTileKeys) : 0;
+
+    // ---- Q of this wave's heads, resident in VGPRs: B operand of S^T = K.Q^T
+    const int h_base = hg * kHPW + hs * 16 * MB;
+    u32x4 qreg[MB][18];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = h_base + mb * 16 + l16;
+        const bool ok = head < a.n_head;
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+            a.q + ((int64_t)row * a.n_head + (ok ? head : a.n_head - 1)) * kDK + 8 * g);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+            u32x4 v = qp[4 * s];
+            if (!ok) v = u32x4{0, 0, 0, 0};
+            if constexpr (kQ8) {
+                if (a.q_bf16) {   // bf16 -> f16 for the f16 MFMA
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = pack_f16x2(bf16_bits_to_f32(v[e] & 0xFFFFu), bf16_bits_to_f32(v[e] >> 16));
+                }
+            }
+            qreg[mb][s] = v;
+        }
+    }
+
+    // ---- online-softmax state, per 16-head block mb (per lane: head l16);
+    // o[mb][nb]: heads 4g..4g+3 of block mb, dv columns 16nb + l16
+    float m_run[MB], l_run[MB];
+    f32x4 o[MB][32];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        m_run[mb] = -INFINITY;
+        l_run[mb] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 32; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- per-lane LDS read offsets (relative to a sub-tile), tile-invariant
+    // S^T A operand: key row (kb*16 + l16), chunk 4*s + g.
+    const int cq = g ^ swz(l16);
+    const int qk_off0 = l16 * kRowBytes16 + 16 * cq;
+    const int qk_off1 = l16 * kRowBytes16 + 16 * (cq ^ 4);
+    // P.V B operand via transpose read: lane 16G + j reads row 4G + j/4 (+16 for the
+    // upper 16 keys), columns 16*nb + 4*(j%4) .. +3 = chunk 2*nb + (j%4)/2, byte 8*(j&1).
+    const int tr_row = 4 * g + (l16 >> 2);
+    const int tr_h = (lane & 3) >> 1;
+    int tr_off[4];
+#pragma unroll
+    for (int nq = 0; nq < 4; ++nq)
+        tr_off[nq] = tr_row * kRowBytes16 + 16 * (((2 * nq) | tr_h) ^ swz(tr_row)) + 8 * (lane & 1);
+
+    // ---- prefetched side data.  idx_next: cache row of list position (tile start +
+    // lane) of the next tile to copy; mask_next / mask_cur: f16 mask bits of key (tile
+    // start + lane) of the tile in flight / being computed.
+    int idx_next = 0;
+    unsigned mask_cur = 0, mask_next = 0;
+    auto load_idx = [&](int it) __attribute__((always_inline)) {
+        if constexpr (IDX) {
+            int64_t pos = k0 + (int64_t)it * kTileKeys + lane;
+            if (pos >= k1) pos = k1 - 1;
+            idx_next = irow[pos];
+        }
+    };
+
+    // Copy tile `it` into stage `st` (HBM -> LDS; raw bytes for Q8_0), then prefetch
+    // the index entries of the tile after it.
+    auto issue_tile = [&](int it, unsigned char *__restrict__ dst) __attribute__((always_inline)) {
+        const int64_t kt = k0 + (int64_t)it * kTileKeys;
+        const int last = (int)((k1 - kt) < kTileKeys ? (k1 - kt) : kTileKeys) - 1;  // last valid row
+        const int my_idx = idx_next;
+        if (mrow) {
+            const int r = lane < last ? lane : last;
+            const int64_t col = IDX ? (int64_t)my_idx : kt + r;
+            mask_next = mrow[IDX ? (int64_t)shfl_int(my_idx, r) : col];
+        }
+        const uint8_t *tbase = IDX ? kvs : kvs + kt * a.kv_row_stride;
+        // recompute the per-lane slot math each tile instead of keeping ~2 VGPRs per
+        // copy alive across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if constexpr (!kQ8) {
+#pragma unroll
+            for (int j = 0; j < kDmaPerTile / NW; ++j) {
+                const int blk = wave + j * NW;                 // 1 KB block of the stage
+                const int slot = blk * 64 + ln;                // 16-byte chunk slot
+                int r = slot / kChunksPerRow;
+                const int lc = (slot - r * kChunksPerRow) ^ swz(r);
+                r = r < last ? r : last;
+                const uint8_t *src;
+                if constexpr (IDX)
+                    src = tbase + (int64_t)shfl_int(my_idx, r) * a.kv_row_stride + lc * 16;
+                else
+                    src = tbase + (uint32_t)(r * (uint32_t)a.kv_row_stride + lc * 16);
+                __builtin_amdgcn_global_load_lds((const void *)src, (LDS_PTR(void))(dst + blk * 1024), 16, 0, 0);
+            }
+        } else {
+            // raw Q8_0 rows of 612 bytes, packed back to back (153 dwords each)
+            constexpr int kDw = kQ8TileBytes / 4;              // 9792 = 153 * 64
+            constexpr int kBlocks = kDw / 64;                  // 153 wave-wide 256 B copies
+#pragma unroll
+            for (int j = 0; j < (kBlocks + NW - 1) / NW; ++j) {
+                const int blk = wave + j * NW;
+                if (blk < kBlocks) {
+                    const int dw = blk * 64 + ln;
+                    int r = dw / (kQ8RowBytes / 4);
+                    const int c = dw - r * (kQ8RowBytes / 4);
+                    r = r < last ? r : last;
+                    const uint8_t *src;
+                    if constexpr (IDX)
+                        src = tbase + (int64_t)shfl_int(my_idx, r) * a.kv_row_stride + c * 4;
+                    else
+                        src = tbase + (uint32_t)(r * (uint32_t)a.kv_row_stride + c * 4);
+                    __builtin_amdgcn_global_load_lds((const void *)src, (LDS_PTR(void))(dst + blk * 256), 4, 0, 0);
+                }
+            }
+        }
+        if (it + 1 < n_tiles) load_idx(it + 1);   // lands together with this tile
+    };
+
+    // Dequantise a raw Q8_0 stage into the f16 tile (same swizzled layout).  One task
+    // = one 34-byte block of one row: f16 scale d at byte 0, 32 int8 codes after it;
+    // value = code * d, computed exactly in fp32 (8-bit code x 11-bit d) and rounded
+    // once to f16.  Blocks are 2-byte aligned; 9 dwords cover one at either phase
+    // (the last block of the last row ends exactly at the end of the raw stage).
+    auto dequant_tile = [&](const unsigned char *raw, unsigned char *f16tile) __attribute__((always_inline)) {
+        const unsigned *rw = reinterpret_cast<const unsigned *>(raw);
+#pragma unroll 1
+        for (int task = threadIdx.x; task < kTileKeys * 18; task += NW * 64) {
+            const int r = task / 18, b = task - (task / 18) * 18;
+            const int byte0 = r * kQ8RowBytes + 34 * b;
+            const bool odd = (byte0 & 2) != 0;                       // block starts mid-dword
+            unsigned w[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) w[i] = rw[(byte0 >> 2) + i];
+            const float d = f16_bits_to_f32((unsigned short)(odd ? (w[0] >> 16) : (w[0] & 0xFFFFu)));
+            const float nd = -128.f * d;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {                                // 8 values -> 16 B chunk
+                unsigned pk[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i = 2 * c + h;                             // code dword i of the block
+                    const unsigned code = odd ? w[i + 1] : __builtin_amdgcn_alignbyte(w[i + 1], w[i], 2);
+                    const unsigned u = code ^ 0x80808080u;               // code + 128 per byte
+                    pk[2 * h] = pack_f16x2(fmaf((float)(u & 0xFFu), d, nd), fmaf((float)((u >> 8) & 0xFFu), d, nd));
+                    pk[2 * h + 1] = pack_f16x2(fmaf((float)((u >> 16) & 0xFFu), d, nd), fmaf((float)(u >> 24), d, nd));
+                }
+                const int lc = 4 * b + c;
+                *reinterpret_cast<u32x4 *>(f16tile + r * kRowBytes16 + 16 * (lc ^ swz(r))) =
+                    u32x4{pk[0], pk[1], pk[2], pk[3]};
+            }
+        }
+    };
+
+    // One 32-key sub-tile: keys sub0..sub0+31 of the tile that starts at key kt.
+    // LDS operands are loaded kQkD / kPvD steps ahead of the MFMAs that use them, and a
+    // scheduling fence closes every step, so at most a few operands are in flight.
+    constexpr int kQkD = 2, kPvD = 3;
+    auto compute_sub = [&](const unsigned char *stage, int64_t kt, int sub0) __attribute__((always_inline)) {
+        const unsigned char *sb = stage + sub0 * kRowBytes16;
+        // S^T = K . Q^T: A = 16 keys x 32 dims from LDS (two 16-key blocks), B = Q
+        f32x4 sacc[2][MB];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) sacc[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 ka[kQkD + 1][2];
+        auto load_k = [&](int s, u32x4 *dst) __attribute__((always_inline)) {
+            const int off = ((s & 1) ? qk_off1 : qk_off0) + 128 * (s >> 1);
+            dst[0] = *reinterpret_cast<const u32x4 *>(sb + off);
+            dst[1] = *reinterpret_cast<const u32x4 *>(sb + off + 16 * kRowBytes16);
+        };
+#pragma unroll
+        for (int s = 0; s < kQkD; ++s) load_k(s, ka[s]);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+            if (s + kQkD < 18) load_k(s + kQkD, ka[(s + kQkD) % (kQkD + 1)]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    sacc[kb][mb] = mfma16x16x32<KIND>(ka[s % (kQkD + 1)][kb], qreg[mb][s], sacc[kb][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // mask bias (log2 units) and validity of this lane's 8 keys:
+        // i < 4: key sub0 + 4g + i; i >= 4: key sub0 + 16 + 4g + (i - 4)
+        float bias[8];
+        bool valid[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = sub0 + 16 * (i >> 2) + 4 * g + (i & 3);
+            valid[i] = kt + kk < k1;
+            bias[i] = 0.f;
+            if (mrow) {
+                const unsigned mb16 = (unsigned)shfl_int((int)mask_cur, kk) & 0xFFFFu;
+                bias[i] = f16_bits_to_f32((unsigned short)mb16) * kLog2e;
+            }
+        }
+        u32x4 pa[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float tv[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = sacc[i >> 2][mb][i & 3] * a.scale_log2 + bias[i];
+                tv[i] = valid[i] ? x : -INFINITY;
+                mx = fmaxf(mx, tv[i]);
+            }
+            mx = wave_max_groups(mx);
+            const bool need = mx > m_run[mb] + kRescaleThresh;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_run[mb] - mx) : 1.f;
+                if (need) m_run[mb] = mx;
+                l_run[mb] *= alpha;
+                float ar[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ar[r] = shfl_f(alpha, 4 * g + r);
+#pragma unroll
+                for (int nb = 0; nb < 32; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[mb][nb][r] *= ar[r];
+            }
+            const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
+            float p[8], ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(tv[i] - m_use);
+                ps += p[i];
+            }
+            l_run[mb] += ps;
+            pa[mb] = u32x4{pack_p<KIND>(p[0], p[1]), pack_p<KIND>(p[2], p[3]),
+                           pack_p<KIND>(p[4], p[5]), pack_p<KIND>(p[6], p[7])};
+        }
+        // O += P . V, V = columns 0..511 of the same rows, transposed on the LDS read
+        u32x4 vb[kPvD + 1];
+        auto load_v = [&](int nb) -> u32x4 __attribute__((always_inline)) {
+            const int off = tr_off[nb & 3] + 128 * (nb >> 2);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off + 16 * kRowBytes16));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+#pragma unroll
+        for (int nb = 0; nb < kPvD; ++nb) vb[nb] = load_v(nb);
+#pragma unroll
+        for (int nb = 0; nb < 32; ++nb) {
+            if (nb + kPvD < 32) vb[(nb + kPvD) % (kPvD + 1)] = load_v(nb + kPvD);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o[mb][nb] = mfma16x16x32<KIND>(pa[mb], vb[nb % (kPvD + 1)], o[mb][nb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // One loop step: start copying tile `it + 1` into `next`, then compute tile `it`
+    // from `cur`.  The stage pointers are restrict-qualified: within a step the copy
+    // target and the tile being read never overlap, which lets the compiler keep the
+    // copy in flight across the LDS reads (without it, every LDS transpose read would
+    // wait for all outstanding copies).  Ordering between steps is explicit: wait for
+    // this wave's copies, then a barrier, at the top of every iteration.
+    auto step16 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur) __attribute__((always_inline)) {
+        if (it + 1 < n_tiles) issue_tile(it + 1, next);
+        const int64_t kt = k0 + (int64_t)it * kTileKeys;
+#pragma unroll 1
+        for (int sub = kp; sub < 2; sub += WK) compute_sub(cur, kt, sub * kSub);
+    };
+    auto stepq8 = [&](int it, unsigned char *__restrict__ next_raw, const unsigned char *__restrict__ raw,
+                      unsigned char *__restrict__ f16tile) __attribute__((always_inline)) {
+        if (it + 1 < n_tiles) issue_tile(it + 1, next_raw);
+        dequant_tile(raw, f16tile);
+        __syncthreads();
+        const int64_t kt = k0 + (int64_t)it * kTileKeys;
+#pragma unroll 1
+        for (int sub = kp; sub < 2; sub += WK) compute_sub(f16tile, kt, sub * kSub);
+    };
+
+    // ---- main loop: one barrier per tile for 16-bit caches (it publishes tile `it`
+    // and frees the other stage), two for Q8_0 (raw copy landed / f16 tile written).
+    if (n_tiles > 0) {
+        load_idx(0);
+        if constexpr (IDX) wait_vm0();
+        issue_tile(0, kQ8 ? lds + kStageBytes : lds);
+        for (int it = 0; it < n_tiles; ++it) {
+            wait_vm0();
+            mask_cur = mask_next;
+            __syncthreads();
+            // one inlined copy of the step with computed stage pointers (two copies
+            // selected by parity would double the register footprint)
+            if constexpr (kQ8) {
+                unsigned char *raw_next = lds + kStageBytes + ((it + 1) & 1) * kQ8TileBytes;
+                const unsigned char *raw_cur = lds + kStageBytes + (it & 1) * kQ8TileBytes;
+                stepq8(it, raw_next, raw_cur, lds);
+            } else {
+                unsigned char *next = lds + ((it + 1) & 1) * kStageBytes;
+                const unsigned char *cur = lds + (it & 1) * kStageBytes;
+                step16(it, next, cur);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) l_run[mb] = wave_sum_groups(l_run[mb]);   // lane groups' sums
+
+    // ---- merge the two key halves of each head set through LDS
+    if constexpr (WK == 2) {
+        __syncthreads();                                   // tiles no longer needed
+        float *xo = reinterpret_cast<float *>(lds) + hs * MB * (32 * 4 * 64 + 32);
+        if (kp == 1) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                float *xb = xo + mb * (32 * 4 * 64 + 32);
+#pragma unroll
+                for (int nb = 0; nb < 32; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) xb[(nb * 4 + r) * 64 + lane] = o[mb][nb][r];
+                if (lane < 16) {
+                    xb[32 * 4 * 64 + lane] = m_run[mb];
+                    xb[32 * 4 * 64 + 16 + lane] = l_run[mb];
+                }
+            }
+        }
+        __syncthreads();
+        if (kp == 1) return;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const float *xb = xo + mb * (32 * 4 * 64 + 32);
+            const float m2 = xb[32 * 4 * 64 + l16], l2 = xb[32 * 4 * 64 + 16 + l16];
+            const float mn = fmaxf(m_run[mb], m2);
+            const float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[mb] - mn);
+            const float a2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+            l_run[mb] = a1 * l_run[mb] + a2 * l2;
+            m_run[mb] = mn;
+            float a1r[4], a2r[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                a1r[r] = shfl_f(a1, 4 * g + r);
+                a2r[r] = shfl_f(a2, 4 * g + r);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 32; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[mb][nb][r] = a1r[r] * o[mb][nb][r] + a2r[r] * xb[(nb * 4 + r) * 64 + lane];
+        }
+    }
+
+    // ---- write the final output (n_split == 1) or this split's partial
+    if (a.n_split == 1) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const float inv = l_run[mb] > 0.f ? 1.f / l_run[mb] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ir = shfl_f(inv, 4 * g + r);
+                const int head = h_base + mb * 16 + 4 * g + r;
+                if (head < a.n_head) {
+                    float *op = a.out + ((int64_t)row * a.n_head + head) * kDV + l16;
+#pragma unroll
+                    for (int nb = 0; nb < 32; ++nb) op[16 * nb] = o[mb][nb][r] * ir;
+                }
+            }
+        }
+    } else {
+        const int64_t RH = (int64_t)n_rows * a.n_head;
+        float *wm = a.ws;
+        float *wl = wm + (int64_t)a.n_split * RH;
+        float *wo = wl + (int64_t)a.n_split * RH;
+        const int64_t base = (int64_t)split * RH + (int64_t)row * a.n_head;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int head_l = h_base + mb * 16 + l16;
+            if (lane < 16 && head_l < a.n_head) {
+                wm[base + head_l] = m_run[mb];
+                wl[base + head_l] = l_run[mb];
+            }
+            if (n_tiles > 0) {              // an empty split leaves O unread by the merge
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int head = h_base + mb * 16 + 4 * g + r;
+                    if (head < a.n_head) {
+                        float *op = wo + (base + head) * kDV + l16;
+#pragma unroll
+                        for (int nb = 0; nb < 32; ++nb) op[16 * nb] = o[mb][nb][r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Merge split partials: out = sum_i 2^(m_i - m*) O_i / sum_i 2^(m_i - m*) l_i; splits with
+// m_i = -inf (no kept key) weigh 0; a row with no kept key anywhere outputs 0.
+__global__ void __launch_bounds__(128) merge_kernel(int n_rows, int n_head, int n_split,
+                                                    const float *__restrict__ ws,
+                                                    float *__restrict__ out) {
+    const int64_t rh = blockIdx.x;                    // row * n_head + head
+    const int64_t RH = (int64_t)n_rows * n_head;
+    const float *wm = ws;
+    const float *wl = wm + (int64_t)n_split * RH;
+    const float *wo = wl + (int64_t)n_split * RH;
+    float mstar = -INFINITY;
+    for (int i = 0; i < n_split; ++i) mstar = fmaxf(mstar, wm[i * RH + rh]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    if (mstar != -INFINITY) {
+        for (int i = 0; i < n_split; ++i) {
+            const float mi = wm[i * RH + rh];
+            if (mi == -INFINITY) continue;
+            const float wgt = __builtin_amdgcn_exp2f(mi - mstar);
+            lsum += wgt * wl[i * RH + rh];
+            const f32x4 v = reinterpret_cast<const f32x4 *>(wo + (i * RH + rh) * kDV)[threadIdx.x];
+            acc += wgt * v;
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    reinterpret_cast<f32x4 *>(out + rh * kDV)[threadIdx.x] = acc * inv;
+}
+
+template <int MB, int NW, int WK, int KIND, bool IDX>
+hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
+    dim3 grid(a.grid_x, a.n_seq * a.n_tok);
+    hipLaunchKernelGGL((attn_kernel<MB, NW, WK, KIND, IDX>), grid, dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int KIND, bool IDX>
+hipError_t launch_shape(const AttnArgs &a, int shape, hipStream_t stream) {
+    switch (shape) {
+        case SHAPE_H16: return launch_one<1, 2, 2, KIND, IDX>(a, stream);
+        case SHAPE_H32: return launch_one<1, 4, 2, KIND, IDX>(a, stream);
+        case SHAPE_H64: return launch_one<1, 8, 2, KIND, IDX>(a, stream);
+        case SHAPE_H128: return launch_one<1, 8, 1, KIND, IDX>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int KIND>
+hipError_t launch_kind(const AttnArgs &a, int shape, hipStream_t stream) {
+    return a.kv_idx ? launch_shape<KIND, true>(a, shape, stream) : launch_shape<KIND, false>(a, shape, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream) {
+    switch (kv_kind) {
+        case KV_BF16: return launch_kind<KV_BF16>(a, shape, stream);
+        case KV_F16: return launch_kind<KV_F16>(a, shape, stream);
+        case KV_Q8: return launch_kind<KV_Q8>(a, shape, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
+                        hipStream_t stream) {
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)n_rows * n_head)), dim3(128), 0,
+                       stream, n_rows, n_head, n_split, ws, out);
+    return hipGetLastError();
+}
+
+}  // namespace mlafa

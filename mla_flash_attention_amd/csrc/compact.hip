@@ -1,0 +1,134 @@
+// compact.hip -- single-scan sparse-mask index compaction for gfx950.
+//
+// For each f16 mask row, write the ascending list of cells whose mask is not -inf and
+// its length.  The scheme follows the sparse-FA commit text ("llama.cpp Vulkan backend
+// adds sparse Flash Attention for quantized K/V", b11413): split the row into
+// contiguous segments, one per subgroup; count the kept cells of each segment with
+// ballots over coalesced loads; one scan over the segment counts gives every segment
+// its output offset; the list stays ascending.  The superseded design (one workgroup
+// walking the row in 1024-cell chunks with a workgroup scan per chunk) is not used.
+//
+// gfx950 specifics: one workgroup of 16 wave64s per row; each lane loads 16 bytes
+// (8 cells) per step, so a wave covers 512 consecutive cells per load.  Per-lane kept
+// counts (0..8) are prefix-summed across the wave with four ballots (one per count
+// bit) and mbcnt, so the scan inside a wave costs no LDS.  The only LDS traffic is
+// the 16 segment counts.  Rows whose base is not 16-byte aligned take a one-cell-per-
+// lane path with the same structure.
+#include "mla_fa_internal.h"
+
+namespace mlafa {
+namespace {
+
+typedef unsigned short u16x8 __attribute__((__vector_size__(16)));
+constexpr int kWaves = 16;
+constexpr unsigned short kNegInf = 0xFC00;
+
+__device__ __forceinline__ unsigned lanes_below(unsigned long long m) {
+    return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// Kept-cell bits (bit e = cell base+e) of the 8 cells a lane covers; cells at or past
+// n_kv count as not kept.
+__device__ __forceinline__ unsigned kept_bits8(const unsigned short *row, int64_t base, int64_t n_kv) {
+    unsigned bits = 0;
+    if (base + 8 <= n_kv) {
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(row + base);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bits |= (unsigned)(v[e] != kNegInf) << e;
+    } else {
+        for (int e = 0; e < 8; ++e)
+            if (base + e < n_kv) bits |= (unsigned)(row[base + e] != kNegInf) << e;
+    }
+    return bits;
+}
+
+// Exclusive prefix (over lanes below) and wave total of per-lane counts c in [0, 15].
+__device__ __forceinline__ void wave_scan4(unsigned c, unsigned &below, unsigned &total) {
+    below = 0;
+    total = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const unsigned long long m = __builtin_amdgcn_ballot_w64((c >> b) & 1u);
+        below += lanes_below(m) << b;
+        total += (unsigned)__builtin_popcountll(m) << b;
+    }
+}
+
+__global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned short *__restrict__ mask,
+                                                              int64_t row_stride, int64_t n_kv,
+                                                              int32_t *__restrict__ idx,
+                                                              int64_t idx_stride,
+                                                              int32_t *__restrict__ count) {
+    __shared__ unsigned seg_count[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned short *row = mask + (int64_t)blockIdx.x * row_stride;
+    int32_t *out = idx + (int64_t)blockIdx.x * idx_stride;
+    const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    const int step = vec ? 512 : 64;                         // cells per wave per load
+    // contiguous segment of this wave, a whole number of load steps
+    int64_t seg = (n_kv + kWaves - 1) / kWaves;
+    seg = (seg + step - 1) / step * step;
+    const int64_t s0 = (int64_t)wave * seg;
+    const int64_t s1 = s0 + seg < n_kv ? s0 + seg : n_kv;
+
+    // pass 1: count this segment's kept cells
+    unsigned my_total = 0;
+    for (int64_t b = s0; b < s1; b += step) {
+        if (vec) {
+            const unsigned k = kept_bits8(row, b + 8 * lane, s1);
+            unsigned below, tot;
+            wave_scan4(__builtin_popcount(k), below, tot);
+            my_total += tot;
+        } else {
+            const int64_t j = b + lane;
+            const bool kept = j < s1 && row[j] != kNegInf;
+            my_total += (unsigned)__builtin_popcountll(__builtin_amdgcn_ballot_w64(kept));
+        }
+    }
+    if (lane == 0) seg_count[wave] = my_total;
+    __syncthreads();
+    // one exclusive scan over the segment counts
+    unsigned offset = 0, all = 0;
+    for (int i = 0; i < kWaves; ++i) {
+        const unsigned c = seg_count[i];
+        offset += i < wave ? c : 0u;
+        all += c;
+    }
+    if (threadIdx.x == 0) count[blockIdx.x] = (int32_t)all;
+
+    // pass 2: write this segment's kept cells, ascending
+    for (int64_t b = s0; b < s1; b += step) {
+        if (vec) {
+            const int64_t base = b + 8 * lane;
+            unsigned k = kept_bits8(row, base, s1);
+            unsigned below, tot;
+            wave_scan4(__builtin_popcount(k), below, tot);
+            unsigned pos = offset + below;
+            while (k) {
+                const int e = __builtin_ctz(k);
+                out[pos++] = (int32_t)(base + e);
+                k &= k - 1;
+            }
+            offset += tot;
+        } else {
+            const int64_t j = b + lane;
+            const bool kept = j < s1 && row[j] != kNegInf;
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(kept);
+            if (kept) out[offset + lanes_below(m)] = (int32_t)j;
+            offset += (unsigned)__builtin_popcountll(m);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                          int32_t *idx, int64_t idx_row_stride, int32_t *count,
+                          hipStream_t stream) {
+    hipLaunchKernelGGL(compact_kernel, dim3(n_rows), dim3(kWaves * 64), 0, stream,
+                       reinterpret_cast<const unsigned short *>(mask), mask_row_stride, n_kv, idx,
+                       idx_row_stride, count);
+    return hipGetLastError();
+}
+
+}  // namespace mlafa

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernel
+// translation units (attn.hip, compact.hip).  Not installed, not part of the ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlafa {
+
+constexpr int kDK = 576;                 // latent 512 + RoPE 64
+constexpr int kDV = 512;                 // V = first 512 columns of the row
+constexpr int kRowBytes16 = kDK * 2;     // an f16/bf16 latent row
+constexpr int kQ8RowBytes = 18 * 34;     // a Q8_0 latent row
+constexpr int kTileKeys = 64;            // keys per LDS-staged tile
+constexpr int kMaxSplits = 1024;
+
+enum KvKind { KV_BF16 = 0, KV_F16 = 1, KV_Q8 = 2 };
+
+// Workgroup shapes: MB 16-head blocks per wave, NW waves, WK waves sharing one head
+// set and splitting each tile's keys between them.  Heads per workgroup =
+// (NW / WK) * 16 * MB.
+enum Shape { SHAPE_H16 = 0, SHAPE_H32 = 1, SHAPE_H64 = 2, SHAPE_H128 = 3 };
+
+struct AttnArgs {
+    const uint16_t *q;             // [n_seq][n_tok][n_head][576]
+    const uint8_t *kv;             // byte base of the cache
+    int64_t kv_row_stride;         // bytes
+    int64_t kv_seq_stride;         // bytes (0 = shared)
+    const uint16_t *mask;          // f16 bits or nullptr
+    int64_t mask_seq_stride;       // elements
+    int64_t mask_tok_stride;       // elements
+    const int32_t *kv_idx;         // sparse index lists or nullptr
+    const int32_t *kv_idx_count;
+    int64_t idx_seq_stride;
+    float *out;                    // [n_seq*n_tok][n_head][512], used when n_split == 1
+    float *ws;                     // partials, used when n_split > 1
+    int64_t n_kv;
+    int64_t split_chunk;           // keys per split for dense rows (multiple of kTileKeys)
+    int n_seq, n_tok, n_head;
+    int causal;
+    int n_split;
+    int head_groups;               // workgroups along the head axis
+    int grid_x;                    // blockIdx.x extent (head_groups * splits, padded)
+    int q_bf16;                    // q bits are bf16 (else f16)
+    float scale_log2;              // scale * log2(e)
+};
+
+// Partial layout inside the workspace, for R = n_seq*n_tok rows, H heads, S splits:
+//   m [S][R][H] fp32 (log2 domain), l [S][R][H] fp32, o [S][R][H][512] fp32.
+inline size_t partial_bytes(int64_t rows, int heads, int splits) {
+    return (size_t)splits * rows * heads * (2 + kDV) * sizeof(float);
+}
+
+hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);
+hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
+                        hipStream_t stream);
+hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                          int32_t *idx, int64_t idx_row_stride, int32_t *count,
+                          hipStream_t stream);
+
+// Heads per workgroup of each shape.
+inline int shape_heads(int shape) { return 16 << shape; }
+
+}  // namespace mlafa

@@ -1,0 +1,122 @@
+"""The C-ABI library: it loads, exports every symbol include/mla_fa.h declares, and its
+host-side validation rejects bad arguments before any HIP call (CPU only: every call
+here returns from the validation layer, no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_flash_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mla_fa.h")).read()
+    return sorted(set(re.findall(r"^(?:const char \*|int |size_t )\s*(\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmlafa.so is not built")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror(L):
+    assert B.mla_fa_version() >= 10000
+    for s in (0, -1, -2, -3, -4):
+        assert B.strerror(s)
+    assert B.strerror(-99) == "unknown status"
+
+
+def test_workspace_and_splits(L):
+    assert B.mla_fa_auto_splits(2048, 128, 4096, B.MLA_FA_BF16) == 1
+    s = B.mla_fa_auto_splits(4, 128, 32768, B.MLA_FA_BF16)
+    assert 1 < s <= 1024
+    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 1) == 0
+    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 8) == 8 * 4 * 128 * 514 * 4
+    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 0) == s * 4 * 128 * 514 * 4
+    assert B.mla_fa_workspace_size(4, 100, 32768, B.MLA_FA_BF16, 8) == 0     # unsupported heads
+
+
+FAKE = 1 << 20    # a 16-byte-aligned non-null address; never dereferenced on these paths
+
+
+def _decode(L, **kw):
+    a = dict(q=FAKE, qt=B.MLA_FA_BF16, kv=FAKE, kvt=B.MLA_FA_BF16, rs=1152, ss=1152 * 64, n_seq=1,
+             H=128, n_kv=64, mask=None, ms=0, idx=None, cnt=None, iss=0, scale=0.1, out=FAKE,
+             n_split=1, ws=None, wsb=0)
+    a.update(kw)
+    return L.mla_fa_decode(a["q"], a["qt"], a["kv"], a["kvt"], a["rs"], a["ss"], a["n_seq"], a["H"],
+                           a["n_kv"], a["mask"], a["ms"], a["idx"], a["cnt"], a["iss"],
+                           ctypes.c_float(a["scale"]), a["out"], a["n_split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.MLA_FA_ERR_INVALID),
+    (dict(kv=None), B.MLA_FA_ERR_INVALID),
+    (dict(out=None), B.MLA_FA_ERR_INVALID),
+    (dict(n_kv=0), B.MLA_FA_ERR_INVALID),
+    (dict(n_kv=1 << 31), B.MLA_FA_ERR_INVALID),
+    (dict(n_seq=0), B.MLA_FA_ERR_INVALID),
+    (dict(H=100), B.MLA_FA_ERR_UNSUPPORTED),
+    (dict(H=144), B.MLA_FA_ERR_UNSUPPORTED),
+    (dict(H=0), B.MLA_FA_ERR_INVALID),
+    (dict(qt=B.MLA_FA_F16), B.MLA_FA_ERR_UNSUPPORTED),        # f16 q with bf16 cache
+    (dict(qt=7), B.MLA_FA_ERR_INVALID),
+    (dict(kvt=9), B.MLA_FA_ERR_INVALID),
+    (dict(q=FAKE + 8), B.MLA_FA_ERR_INVALID),                   # misaligned q
+    (dict(rs=1000), B.MLA_FA_ERR_INVALID),                      # row stride < row bytes
+    (dict(rs=1160), B.MLA_FA_ERR_INVALID),                      # not a multiple of 16
+    (dict(ss=-16), B.MLA_FA_ERR_INVALID),
+    (dict(scale=float("inf")), B.MLA_FA_ERR_INVALID),
+    (dict(scale=float("nan")), B.MLA_FA_ERR_INVALID),
+    (dict(idx=FAKE), B.MLA_FA_ERR_INVALID),                     # index list without count
+    (dict(n_split=-1), B.MLA_FA_ERR_INVALID),
+    (dict(n_split=1025), B.MLA_FA_ERR_INVALID),
+    (dict(n_split=4), B.MLA_FA_ERR_WORKSPACE),                  # split without a workspace
+    (dict(n_split=4, ws=FAKE, wsb=16), B.MLA_FA_ERR_WORKSPACE), # workspace too small
+    (dict(n_seq=2, mask=FAKE, ms=10), B.MLA_FA_ERR_INVALID),    # mask rows overlap
+    (dict(kvt=B.MLA_FA_Q8_0, rs=600), B.MLA_FA_ERR_INVALID),    # Q8_0 row is 612 bytes
+    (dict(kvt=B.MLA_FA_Q8_0, rs=614), B.MLA_FA_ERR_INVALID),    # Q8_0 stride not 4-aligned
+])
+def test_decode_validation(L, kw, status):
+    assert _decode(L, **kw) == status
+
+
+def test_prefill_validation(L):
+    f = lambda **kw: L.mla_fa_prefill(kw.get("q", FAKE), B.MLA_FA_BF16, FAKE, B.MLA_FA_BF16, 1152,
+                                      kw.get("n_tok", 8), 128, kw.get("n_kv", 16), kw.get("causal", 1),
+                                      None, 0, ctypes.c_float(0.1), FAKE, 1, None, 0, None)
+    assert f(n_tok=17, n_kv=16) == B.MLA_FA_ERR_INVALID            # causal chunk longer than cache
+    assert f(q=None) == B.MLA_FA_ERR_INVALID
+    assert f(n_tok=0) == B.MLA_FA_ERR_INVALID
+
+
+def test_compact_validation(L):
+    f = lambda m=FAKE, ms=100, rows=1, n=100, idx=FAKE, istr=100, cnt=FAKE: L.fa_mask_compact(
+        m, ms, rows, n, idx, istr, cnt, None)
+    assert f(m=None) == B.MLA_FA_ERR_INVALID
+    assert f(idx=None) == B.MLA_FA_ERR_INVALID
+    assert f(cnt=None) == B.MLA_FA_ERR_INVALID
+    assert f(istr=99) == B.MLA_FA_ERR_INVALID
+    assert f(rows=2, ms=50) == B.MLA_FA_ERR_INVALID
+    assert f(n=0) == B.MLA_FA_ERR_INVALID
+    assert f(m=FAKE + 1) == B.MLA_FA_ERR_INVALID
+
+
+def test_merge_validation(L):
+    assert L.mla_fa_merge_partials(4, 128, 8, FAKE, None, 0, None) == B.MLA_FA_ERR_WORKSPACE
+    assert L.mla_fa_merge_partials(4, 100, 8, FAKE, FAKE, 1 << 30, None) == B.MLA_FA_ERR_UNSUPPORTED
+    assert L.mla_fa_merge_partials(0, 128, 8, FAKE, FAKE, 1 << 30, None) == B.MLA_FA_ERR_INVALID
+    # n_split == 1 has nothing to merge
+    assert L.mla_fa_merge_partials(4, 128, 1, FAKE, None, 0, None) == B.MLA_FA_OK

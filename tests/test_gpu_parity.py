@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.  Attention outputs must satisfy, over the whole output tensor, relative L2 error
+<= 5e-3 and max |error| <= 2e-2; compacted index lists and counts must be bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+from mla_flash_attention_amd import synth
+from tests.gpu_common import assert_parity, run_decode, run_prefill, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BF16, F16, Q8 = synth.TYPE_BF16, synth.TYPE_F16, synth.TYPE_Q8_0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from mla_flash_attention_amd import binding
+    binding.lib()
+
+
+def _decode_case(n_seq, n_head, n_kv, q_type, kv_type, seed, n_split=0, mask_kind=None, q_gain=1.0):
+    p = synth.make_problem(kind="decode", n_seq=n_seq, n_head=n_head, n_kv=n_kv, q_type=q_type,
+                           kv_type=kv_type, seed=seed, mask_kind=mask_kind, q_gain=q_gain)
+    got, _ = run_decode(p, n_split=n_split)
+    ref = oracle.attention_problem(p)
+    return assert_parity(got, ref, f"decode s{n_seq} h{n_head} kv{n_kv} t{q_type}/{kv_type} split{n_split}")
+
+
+# ---------------------------------------------------------------- workloads at full size
+def test_c1_full():
+    p = synth.make_config(1)
+    for n_split in (0, 1):
+        got, _ = run_decode(p, n_split=n_split)
+        assert_parity(got, oracle.attention_problem(p), f"C1 split{n_split}")
+
+
+def test_c2_full():
+    p = synth.make_config(2)
+    got, _ = run_decode(p)
+    assert_parity(got, oracle.attention_problem(p), "C2")
+
+
+def test_c4_full():
+    p = synth.make_config(4)
+    got, _ = run_decode(p)
+    assert_parity(got, oracle.attention_problem(p), "C4")
+
+
+def test_c5_full_sparse():
+    p = synth.make_config(5)
+    got, ex = run_decode(p)
+    idx_ref, cnt_ref = oracle.mask_compact(p.mask.reshape(1, -1))
+    cnt = int(ex["count"].cpu()[0])
+    assert cnt == int(cnt_ref[0])
+    assert np.array_equal(ex["idx"].cpu().numpy()[0, :cnt], idx_ref[0, :cnt])
+    assert_parity(got, oracle.attention_problem(p), "C5")
+
+
+def test_c3_full_sampled_rows():
+    """Full prefill; rows checked: first/last tokens, tile edges, random tokens."""
+    p = synth.make_config(3)
+    got = run_prefill(p)
+    toks = sorted({0, 1, 63, 64, 65, 1023, 1024, 2046, 2047} |
+                  set(np.random.default_rng(0).integers(0, 2048, 8).tolist()))
+    rows = np.array([t * 128 + h for t in toks for h in range(128)])
+    ref = oracle.attention_problem(p, rows=rows)
+    assert_parity(got[rows], ref, "C3 sampled tokens")
+
+
+# ---------------------------------------------------------------- reduced-size sweeps
+@pytest.mark.parametrize("n_kv", [1, 2, 31, 32, 33, 63, 64, 65, 1000, 4097])
+@pytest.mark.parametrize("n_head", [16, 128])
+def test_decode_kv_sweep(n_kv, n_head):
+    _decode_case(2, n_head, n_kv, BF16, BF16, seed=n_kv + n_head)
+
+
+@pytest.mark.parametrize("n_head", [16, 32, 48, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("kv_type", [BF16, F16])
+def test_decode_head_counts(n_head, kv_type):
+    _decode_case(2, n_head, 777, kv_type, kv_type, seed=n_head)
+
+
+@pytest.mark.parametrize("n_split", [1, 2, 3, 0, 1024])
+def test_decode_split_sweep(n_split):
+    _decode_case(3, 128, 5000, BF16, BF16, seed=40 + n_split, n_split=n_split)
+
+
+@pytest.mark.parametrize("q_type", [BF16, F16])
+@pytest.mark.parametrize("n_kv", [1, 65, 3000])
+def test_decode_q8_0(q_type, n_kv):
+    _decode_case(2, 128, n_kv, q_type, Q8, seed=7 + n_kv)
+
+
+@pytest.mark.parametrize("mask_kind", ["random", "runs_bias"])
+@pytest.mark.parametrize("kv_type", [BF16, Q8])
+def test_decode_masked_dense(mask_kind, kv_type):
+    q_type = BF16
+    _decode_case(3, 64, 2500, q_type, kv_type, seed=11, mask_kind=mask_kind)
+
+
+@pytest.mark.parametrize("kv_type", [BF16, F16, Q8])
+@pytest.mark.parametrize("mask_kind", ["runs", "runs_bias", "random"])
+def test_decode_sparse_reduced(kv_type, mask_kind):
+    q_type = F16 if kv_type == F16 else BF16
+    p = synth.make_problem(kind="sparse", n_seq=2, n_head=128, n_kv=20000, q_type=q_type,
+                           kv_type=kv_type, seed=3, mask_kind=mask_kind)
+    got, ex = run_decode(p)
+    idx_ref, cnt_ref = oracle.mask_compact(p.mask.reshape(2, -1))
+    cnt = ex["count"].cpu().numpy()
+    assert np.array_equal(cnt, cnt_ref)
+    idx = ex["idx"].cpu().numpy()
+    for s in range(2):
+        assert np.array_equal(idx[s, :cnt[s]], idx_ref[s, :cnt[s]])
+    assert_parity(got, oracle.attention_problem(p), f"sparse {kv_type} {mask_kind}")
+
+
+@pytest.mark.parametrize("n_tok,n_kv", [(1, 1), (5, 7), (64, 64), (70, 300), (128, 1000)])
+def test_prefill_causal_reduced(n_tok, n_kv):
+    p = synth.make_problem(kind="prefill", n_tok=n_tok, n_head=128, n_kv=n_kv, seed=n_kv, causal=True)
+    assert_parity(run_prefill(p), oracle.attention_problem(p), f"prefill {n_tok}x{n_kv}")
+
+
+def test_prefill_split_and_mask():
+    p = synth.make_problem(kind="prefill", n_tok=6, n_head=16, n_kv=3000, seed=8, causal=True,
+                           mask_kind="random")
+    for n_split in (0, 1, 5):
+        assert_parity(run_prefill(p, n_split=n_split), oracle.attention_problem(p), f"prefill split{n_split}")
+
+
+def test_prefill_noncausal_q8():
+    p = synth.make_problem(kind="prefill", n_tok=33, n_head=32, n_kv=500, seed=9, causal=False,
+                           kv_type=Q8, q_type=F16)
+    assert_parity(run_prefill(p), oracle.attention_problem(p), "prefill non-causal q8_0")
+
+
+# ---------------------------------------------------------------- adversarial softmax
+def _bf(x):
+    return synth.round_bits(np.asarray(x, np.float32), BF16)
+
+
+def test_scores_rise_every_tile():
+    """Each 64-key tile raises the running max by ~14 (~20 in log2 units), so every tile
+    rescales.  The rising component sits in a RoPE column (575), outside V, so outputs
+    keep the N(0,1) scale the absolute tolerance is meant for."""
+    p = synth.make_problem(kind="decode", n_seq=1, n_head=16, n_kv=700, seed=50)
+    p.q[..., 575] = _bf(60.0)
+    p.kv[0, :, 575] = _bf(0.05 * np.arange(700))
+    assert_parity(run_decode(p, n_split=1)[0], oracle.attention_problem(p), "rising")
+
+
+def test_planted_peak_last_key():
+    p = synth.make_problem(kind="decode", n_seq=1, n_head=16, n_kv=1000, seed=51, q_gain=3.0)
+    p.kv[0, -1] = p.q[0, 0, 3]                   # the last key equals head 3's query
+    assert_parity(run_decode(p, n_split=2)[0], oracle.attention_problem(p), "peak")
+
+
+def test_all_keys_equal():
+    p = synth.make_problem(kind="decode", n_seq=1, n_head=16, n_kv=300, seed=52)
+    p.kv[0, :] = p.kv[0, 0]
+    got = run_decode(p)[0]
+    assert_parity(got, oracle.attention_problem(p), "equal keys")
+
+
+def test_all_masked_but_one_and_fully_masked():
+    p = synth.make_problem(kind="decode", n_seq=2, n_head=16, n_kv=900, seed=53, mask_kind="none_kept")
+    p.mask[0, 0, 417] = 0                        # sequence 0 keeps one cell, sequence 1 none
+    for sparse in (False, True):
+        got, _ = run_decode(p, via_compaction=sparse)
+        ref = oracle.attention_problem(p)
+        assert np.all(got[16:] == 0.0)           # fully masked row -> zeros, not NaN
+        assert_parity(got, ref, f"one kept (sparse={sparse})")
+
+
+# ---------------------------------------------------------------- determinism and redzones
+def test_bitwise_determinism():
+    p = synth.make_config(2, n_kv=9000)
+    a, _ = run_decode(p)
+    b, _ = run_decode(p)
+    assert np.array_equal(a, b)
+
+
+def test_redzones_untouched():
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="decode", n_seq=2, n_head=128, n_kv=3000, seed=60)
+    pad = 4096
+    buf = torch.full((2 * 128 * 512 + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    out = buf[pad:pad + 2 * 128 * 512].view(2, 128, 512)
+    nsplit = 6
+    ws_bytes = B.mla_fa_workspace_size(2, 128, 3000, BF16, nsplit)
+    wbuf = torch.full((ws_bytes + 2 * pad,), 77, dtype=torch.uint8, device="cuda")
+    ws = wbuf[pad:pad + ws_bytes]
+    got, _ = run_decode(p, n_split=nsplit, out=out, ws=ws)
+    assert_parity(got, oracle.attention_problem(p), "redzone run")
+    assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+    assert torch.all(wbuf[:pad] == 77) and torch.all(wbuf[-pad:] == 77)
+
+
+# ---------------------------------------------------------------- compaction
+@pytest.mark.parametrize("case", ["empty", "full", "first", "last", "alternating", "runs", "tiny"])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_compaction_cases(case, aligned):
+    import torch
+    from mla_flash_attention_amd import binding as B
+    n = 3 if case == "tiny" else 70001
+    g = np.random.default_rng(5)
+    rows = []
+    for r in range(3):
+        bits = np.full(n, synth.F16_NEG_INF, np.uint16)
+        if case == "full":
+            bits[:] = 0
+        elif case == "first":
+            bits[0] = 0
+        elif case == "last":
+            bits[-1] = 0
+        elif case == "alternating":
+            bits[r % 2::2] = 0x3C00
+        elif case in ("runs", "tiny"):
+            bits = synth.sparse_runs_mask(n, g, max_gap=700 if n > 3 else 1, max_run=600 if n > 3 else 1)
+        rows.append(bits)
+    m = np.stack(rows)
+    # aligned: rows start on 16-byte boundaries (vector path); unaligned: the buffer is
+    # offset by one element and rows are n + 3 apart (one-cell-per-lane path)
+    stride = n + 8 - n % 8 if aligned else n + 3
+    lead = 0 if aligned else 1
+    host = np.full(lead + 3 * stride, 0x1234, np.uint16)
+    host[lead:].reshape(3, stride)[:, :n] = m
+    mask = to_dev(host)[lead:].view(3, stride)[:, :n]
+    idx = torch.full((3, n + 5), -9, dtype=torch.int32, device="cuda")
+    cnt = torch.full((3,), -9, dtype=torch.int32, device="cuda")
+    B.fa_mask_compact(mask, idx, cnt)
+    torch.cuda.synchronize()
+    idx_ref, cnt_ref = oracle.mask_compact(m)
+    ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(ci, cnt_ref)
+    for r in range(3):
+        assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
+        assert np.all(ii[r, ci[r]:] == -9)        # untouched past the count
