@@ -1,0 +1,272 @@
+"""Benchmark: MLA flash-attention decode over the latent cache on one MI355X.
+
+Headline workload: 4 sequences x 1 query token x 128 heads, each with its own latent
+cache of 32768 rows x 576 bf16 (DeepSeek-V3 head count), split-KV with a partial
+(m, l, O) merge.  A step is one mla_fa_decode call (split attention + merge) with
+every input already resident in HBM.  Timed steps rotate over 4 copies of the inputs
+(4 x 151 MB, more than the 256 MB last-level cache) so every step reads the cache from
+HBM.  Prints one JSON line (see the repository's bench contract).
+
+Secondary lines (same JSON object, key "secondary"): the other workloads - 16-head
+f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 MFMA, published
+ROW_BYTES = {1: 1152, 2: 1152, 3: 612}
+METRIC = "MLA FA latent KV cells/s per GPU + % of HBM / MFMA roofline"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="rotating input copies (cold cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", default="", help="run only these workloads, e.g. 'c2' or 'c3,c4'")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h"):
+        with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), or None when the
+    counters are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != _source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def _time_decode(B, p, copies, steps, warmup, n_split=0, split_phases=True):
+    """Per-step split-attention and merge durations (events on the launch stream)."""
+    import torch
+    from mla_flash_attention_amd import synth
+    stream = torch.cuda.current_stream()
+    qs, kvs = [], []
+    for c in range(copies):
+        qs.append(_dev(p.q.reshape(p.n_seq, p.n_head, synth.DK)))
+        kvs.append(_dev(p.kv))
+    mask = None if p.mask is None else _dev(p.mask.reshape(p.n_seq, p.n_kv))
+    out = torch.empty((p.n_seq, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    ns = n_split or B.mla_fa_auto_splits(p.n_seq, p.n_head, p.n_kv, p.kv_type)
+    ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, ns)
+    sparse = p.kind == "sparse"
+    idx = cnt = None
+    if sparse:
+        idx = torch.empty((p.n_seq, p.n_kv), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((p.n_seq,), dtype=torch.int32, device="cuda")
+
+    def step(i, ev=None):
+        c = i % copies
+        if ev is not None:
+            ev[0].record(stream)
+        if sparse:
+            B.fa_mask_compact(mask, idx, cnt, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        B.mla_fa_decode_partials(qs[c], p.q_type, kvs[c], p.kv_type, p.scale, out, mask=mask,
+                                 kv_idx=idx, kv_idx_count=cnt, n_split=ns, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        if ns > 1:
+            B.mla_fa_merge_partials(p.n_seq, p.n_head, ns, out, ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    compact_ms = [e[0].elapsed_time(e[1]) for e in evs] if sparse else None
+    part_ms = [(e[1] if sparse else e[0]).elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    kept = int(cnt.cpu()[0]) if sparse else None
+    return dict(total_ms=total_ms, step_ms=total_ms / steps, part_ms=float(np.mean(part_ms)),
+                part_ms_p10=float(np.percentile(part_ms, 10)), part_ms_p90=float(np.percentile(part_ms, 90)),
+                merge_ms=float(np.mean(merge_ms)),
+                compact_ms=None if compact_ms is None else float(np.mean(compact_ms)),
+                n_split=ns, kept=kept)
+
+
+def _time_prefill(B, p, steps, warmup):
+    import torch
+    from mla_flash_attention_amd import synth
+    stream = torch.cuda.current_stream()
+    q = _dev(p.q.reshape(p.n_tok, p.n_head, synth.DK))
+    kv = _dev(p.kv.reshape(p.n_kv, -1))
+    out = torch.empty((p.n_tok, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        B.mla_fa_prefill(q, p.q_type, kv, p.kv_type, p.scale, out, causal=True, n_split=1, stream=stream)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        B.mla_fa_prefill(q, p.q_type, kv, p.kv_type, p.scale, out, causal=True, n_split=1, stream=stream)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(step_ms=float(np.mean(ms)), p10=float(np.percentile(ms, 10)), p90=float(np.percentile(ms, 90)))
+
+
+def _algo_decode(p, kept=None):
+    """Algorithmic bytes and flops of one decode call: cache rows attended, Q, O (and the
+    mask/index traffic of the sparse path); flops 2*H*(576+512) per attended cell."""
+    cells = p.n_seq * (kept if kept is not None else p.n_kv)
+    row = ROW_BYTES[p.kv_type]
+    qb = p.n_seq * p.n_head * 576 * 2
+    ob = p.n_seq * p.n_head * 512 * 4
+    kernel_bytes = cells * row + qb                      # what the attention kernel must read
+    call_bytes = kernel_bytes + ob
+    if kept is not None:
+        call_bytes += 2 * p.n_kv * p.n_seq + (4 + 4 + 2) * cells
+    flops = cells * 2 * p.n_head * (576 + 512)
+    return cells, kernel_bytes, call_bytes, flops
+
+
+def _cpu_baseline(p, limit_s=40.0):
+    """The fp64 oracle on the host cores over the full workload (it finishes in seconds
+    there); cells/s."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.attention_problem(p)
+    dt = time.perf_counter() - t0
+    return dict(value=p.n_seq * p.n_kv / dt, unit="cells/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"the whole workload ({p.n_seq} seq x {p.n_kv} cells x {p.n_head} heads, fp64), "
+                       f"{dt:.2f} s wall", seconds=round(dt, 3))
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is design-only in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mla_flash_attention_amd import binding as B
+    from mla_flash_attention_amd import synth
+    B.lib()
+    only = set(x.strip().lower() for x in args.only.split(",") if x.strip())
+    want = lambda k: not only or k in only
+
+    result = {}
+    if want("c2"):
+        p2 = synth.make_config(2)
+        r = _time_decode(B, p2, args.copies, args.steps, args.warmup)
+        cells, kbytes, cbytes, flops = _algo_decode(p2)
+        value = cells / (r["step_ms"] * 1e-3)
+        achieved = kbytes / (r["part_ms"] * 1e-3) / 1e9
+        result = {
+            "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic: seeded N(0,1) rounded to bf16, DeepSeek-V3 MLA shapes",
+            "config": {"workload": "MLA decode, 4 seq x 1 token x 128 heads, latent cache n_kv=32768 x 576 bf16 "
+                                   "per sequence, split-KV + merge", "n_seq": 4, "n_head": 128,
+                       "n_kv": 32768, "n_split": r["n_split"], "input_copies": args.copies},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic("decode_c2"),
+                         "kernel": "attn_kernel (split attention)", "kernel_ms": r["part_ms"],
+                         "kernel_ms_p10": r["part_ms_p10"], "kernel_ms_p90": r["part_ms_p90"],
+                         "algorithmic_bytes": kbytes, "merge_ms": r["merge_ms"],
+                         "mfma_tflops": flops / (r["part_ms"] * 1e-3) / 1e12,
+                         "mfma_frac": flops / (r["part_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "call_frac_hbm": cbytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        }
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = _cpu_baseline(p2)
+    sec = {}
+    if not args.no_secondary:
+        if want("c1"):
+            p = synth.make_config(1)
+            r = _time_decode(B, p, 1, args.steps, args.warmup)
+            cells, kb, cb, fl = _algo_decode(p)
+            sec["c1_decode_16h_f16_warm"] = dict(ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3),
+                                                 kernel_ms=r["part_ms"], n_split=r["n_split"])
+        if want("c3"):
+            p = synth.make_config(3)
+            r = _time_prefill(B, p, max(5, args.steps // 5), max(2, args.warmup // 5))
+            pairs = sum(p.n_kv - p.n_tok + t + 1 for t in range(p.n_tok))
+            fl = pairs * 2 * p.n_head * (576 + 512)
+            tf = fl / (r["step_ms"] * 1e-3) / 1e12
+            sec["c3_prefill_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
+                                                      cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
+                                                      mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
+        if want("c4"):
+            p = synth.make_config(4)
+            r = _time_decode(B, p, args.copies, args.steps, args.warmup)
+            cells, kb, cb, fl = _algo_decode(p)
+            tf = fl / (r["part_ms"] * 1e-3) / 1e12
+            sec["c4_decode_q8_0"] = dict(ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3),
+                                         kernel_ms=r["part_ms"], merge_ms=r["merge_ms"], n_split=r["n_split"],
+                                         hbm_frac=kb / (r["part_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                         mfma_tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS)
+        if want("c5"):
+            p = synth.make_config(5)
+            r = _time_decode(B, p, 1, args.steps, args.warmup)
+            cells, kb, cb, fl = _algo_decode(p, kept=r["kept"])
+            sec["c5_sparse_131072_cells"] = dict(ms=r["step_ms"], compact_ms=r["compact_ms"],
+                                                 attn_ms=r["part_ms"], merge_ms=r["merge_ms"],
+                                                 kept=r["kept"], n_split=r["n_split"],
+                                                 scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
+                                                 kept_cells_per_s=r["kept"] / (r["step_ms"] * 1e-3))
+    if sec:
+        result["secondary"] = sec
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result.setdefault("calibration", {})["copy_bytes"] = n
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,7 +182,7 @@ def make_problem(kind: str = "decode", n_seq: int = 1, n_tok: int = 1, n_head: i
     kf = gk.standard_normal((n_kv_seqs, n_kv, dk), dtype=np.float32)
     q_bits = round_bits(qf, q_type)
     kv = quantize_q8_0(kf) if kv_type == TYPE_Q8_0 else round_bits(kf, kv_type)
-    if sparse and mask_kind is None:
+    if (sparse or kind == "sparse") and mask_kind is None:
         mask_kind = "runs"
     mask = make_mask(mask_kind, n_seq, n_tok, n_kv, gm)
     return Problem(name=name or f"{kind} s{n_seq} t{n_tok} h{n_head} kv{n_kv}", kind=kind,
