@@ -51,6 +51,14 @@ int env_splits() {
 // key halves merge in LDS (half the partial bytes of 128-head workgroups); unsplit
 // calls use 128-head workgroups so each tile is read once per query row.
 int pick_shape(int n_head, int n_split) {
+    if (const char *e = std::getenv("MLA_FA_SHAPE")) {       // tuning only
+        switch (std::atoi(e)) {
+            case 16: return SHAPE_H16;
+            case 32: return SHAPE_H32;
+            case 64: return SHAPE_H64;
+            case 128: return SHAPE_H128;
+        }
+    }
     if (n_head <= 16) return SHAPE_H16;
     if (n_head <= 32) return SHAPE_H32;
     if (n_head <= 64 || n_split > 1) return SHAPE_H64;

@@ -17,8 +17,8 @@
 //
 // Design (gfx950-specific, not from the pages):
 //   * 64-key tiles of 576-wide rows are copied HBM -> LDS with global_load_lds_dwordx4
-//     (no VGPR staging), double-buffered, 16-byte chunks XOR-swizzled per row so both
-//     LDS read patterns below are bank-conflict free.  Q8_0 tiles are DMA'd raw and
+//     (no VGPR staging), double-buffered, rows padded to a 1184-byte pitch so both LDS
+//     read patterns below are bank-conflict free.  Q8_0 tiles are DMA'd raw and
 //     dequantised LDS -> LDS to f16.
 //   * Q.K^T runs as S^T = K.Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys from
 //     LDS, B = 16 heads of Q held in VGPRs for the whole kernel.  The accumulator
@@ -45,17 +45,18 @@ typedef unsigned u32x2 __attribute__((__vector_size__(8)));
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
 constexpr int kSub = 32;                                  // keys per compute sub-tile
-constexpr int kTileBytes = kTileKeys * kRowBytes16;       // 73,728
-constexpr int kChunksPerRow = kRowBytes16 / 16;           // 72
-constexpr int kDmaPerTile = kTileBytes / 1024;            // 72 wave-wide 1 KB copies
+// An LDS tile row is the 1152-byte latent row plus 32 bytes of padding: with a 1184-byte
+// pitch (= 32 mod 256) both read patterns below are bank-conflict free on gfx950
+// (measured: 1152-byte pitch runs the S^T reads at ~1/4 and the transpose reads at ~1/3
+// of the padded rate).
+constexpr int kLdsRow = kRowBytes16 + 32;                 // 1184
+constexpr int kChunksPerLdsRow = kLdsRow / 16;            // 74 (72 data + 2 pad)
+constexpr int kTileBytes = kTileKeys * kLdsRow;           // 75,776
+constexpr int kDmaPerTile = kTileBytes / 1024;            // 74 wave-wide 1 KB copies
+static_assert(kTileBytes % 1024 == 0, "whole 1 KB copies per tile");
 constexpr int kQ8TileBytes = kTileKeys * kQ8RowBytes;     // 39,168
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThresh = 8.0f;                    // log2 units
-
-// Row r's 16-byte chunk c lives at chunk (c ^ swz(r)) of that row.  swz permutes the
-// low three chunk bits so that (a) 8 consecutive rows at one chunk and (b) 4
-// consecutive rows at two adjacent chunks fall into distinct LDS banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <typename T> __device__ __forceinline__ T bitcast_to(u32x4 v) {
     return __builtin_bit_cast(T, v);
@@ -133,7 +134,6 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     constexpr int kF16Stages = kQ8 ? 1 : 2;
     constexpr int kLdsBytes = kF16Stages * kStageBytes + (kQ8 ? 2 * kQ8TileBytes : 0);
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-    static_assert(kDmaPerTile % NW == 0, "tile copies split evenly over waves");
     static_assert(WK == 1 || kHS * MB * (32 * 4 * 64 + 32) * 4 <= kLdsBytes, "key-half merge fits in LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
 
@@ -218,18 +218,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     }
 
     // ---- per-lane LDS read offsets (relative to a sub-tile), tile-invariant
-    // S^T A operand: key row (kb*16 + l16), chunk 4*s + g.
-    const int cq = g ^ swz(l16);
-    const int qk_off0 = l16 * kRowBytes16 + 16 * cq;
-    const int qk_off1 = l16 * kRowBytes16 + 16 * (cq ^ 4);
+    // S^T A operand: key row (kb*16 + l16), dims 32*s + 8*g .. +7 (byte 64*s + 16*g).
+    const int qk_off = l16 * kLdsRow + 16 * g;
     // P.V B operand via transpose read: lane 16G + j reads row 4G + j/4 (+16 for the
-    // upper 16 keys), columns 16*nb + 4*(j%4) .. +3 = chunk 2*nb + (j%4)/2, byte 8*(j&1).
-    const int tr_row = 4 * g + (l16 >> 2);
-    const int tr_h = (lane & 3) >> 1;
-    int tr_off[4];
-#pragma unroll
-    for (int nq = 0; nq < 4; ++nq)
-        tr_off[nq] = tr_row * kRowBytes16 + 16 * (((2 * nq) | tr_h) ^ swz(tr_row)) + 8 * (lane & 1);
+    // upper 16 keys), columns 16*nb + 4*(j%4) .. +3 (byte 32*nb + 8*(j%4)).
+    const int tr_off = (4 * g + (l16 >> 2)) * kLdsRow + 8 * (lane & 3);
 
     // ---- prefetched side data.  idx_next: cache row of list position (tile start +
     // lane) of the next tile to copy; mask_next / mask_cur: f16 mask bits of key (tile
@@ -262,11 +255,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         asm volatile("" : "+v"(ln));
         if constexpr (!kQ8) {
 #pragma unroll
-            for (int j = 0; j < kDmaPerTile / NW; ++j) {
+            for (int j = 0; j < (kDmaPerTile + NW - 1) / NW; ++j) {
                 const int blk = wave + j * NW;                 // 1 KB block of the stage
+                if (kDmaPerTile % NW != 0 && blk >= kDmaPerTile) break;
                 const int slot = blk * 64 + ln;                // 16-byte chunk slot
-                int r = slot / kChunksPerRow;
-                const int lc = (slot - r * kChunksPerRow) ^ swz(r);
+                int r = slot / kChunksPerLdsRow;
+                int lc = slot - r * kChunksPerLdsRow;
+                lc = lc < 72 ? lc : lc - 2;                    // pad slots re-fetch chunks 70/71
                 r = r < last ? r : last;
                 const uint8_t *src;
                 if constexpr (IDX)
@@ -328,7 +323,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     pk[2 * h + 1] = pack_f16x2(fmaf((float)((u >> 16) & 0xFFu), d, nd), fmaf((float)(u >> 24), d, nd));
                 }
                 const int lc = 4 * b + c;
-                *reinterpret_cast<u32x4 *>(f16tile + r * kRowBytes16 + 16 * (lc ^ swz(r))) =
+                *reinterpret_cast<u32x4 *>(f16tile + r * kLdsRow + 16 * lc) =
                     u32x4{pk[0], pk[1], pk[2], pk[3]};
             }
         }
@@ -339,7 +334,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // scheduling fence closes every step, so at most a few operands are in flight.
     constexpr int kQkD = 2, kPvD = 3;
     auto compute_sub = [&](const unsigned char *stage, int64_t kt, int sub0) __attribute__((always_inline)) {
-        const unsigned char *sb = stage + sub0 * kRowBytes16;
+        const unsigned char *sb = stage + sub0 * kLdsRow;
         // S^T = K . Q^T: A = 16 keys x 32 dims from LDS (two 16-key blocks), B = Q
         f32x4 sacc[2][MB];
 #pragma unroll
@@ -348,9 +343,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             for (int mb = 0; mb < MB; ++mb) sacc[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x4 ka[kQkD + 1][2];
         auto load_k = [&](int s, u32x4 *dst) __attribute__((always_inline)) {
-            const int off = ((s & 1) ? qk_off1 : qk_off0) + 128 * (s >> 1);
+            const int off = qk_off + 64 * s;
             dst[0] = *reinterpret_cast<const u32x4 *>(sb + off);
-            dst[1] = *reinterpret_cast<const u32x4 *>(sb + off + 16 * kRowBytes16);
+            dst[1] = *reinterpret_cast<const u32x4 *>(sb + off + 16 * kLdsRow);
         };
 #pragma unroll
         for (int s = 0; s < kQkD; ++s) load_k(s, ka[s]);
@@ -416,10 +411,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         }
         // O += P . V, V = columns 0..511 of the same rows, transposed on the LDS read
         u32x4 vb[kPvD + 1];
-        auto load_v = [&](int nb) -> u32x4 __attribute__((always_inline)) {
-            const int off = tr_off[nb & 3] + 128 * (nb >> 2);
+        auto load_v = [&](int nb) __attribute__((always_inline)) -> u32x4 {
+            const int off = tr_off + 32 * nb;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off + 16 * kRowBytes16));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off + 16 * kLdsRow));
             const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
@@ -571,31 +566,70 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
 }
 
 // Merge split partials: out = sum_i 2^(m_i - m*) O_i / sum_i 2^(m_i - m*) l_i; splits with
-// m_i = -inf (no kept key) weigh 0; a row with no kept key anywhere outputs 0.
-__global__ void __launch_bounds__(128) merge_kernel(int n_rows, int n_head, int n_split,
-                                                    const float *__restrict__ ws,
-                                                    float *__restrict__ out) {
+// m_i = -inf (no kept key) weigh 0 and their O_i is never read; a row with no kept key
+// anywhere outputs 0.  One workgroup per (row, head): the per-split (m, l) are loaded
+// in parallel into LDS, then each thread streams its 4 dv columns of every split's O
+// with several independent loads in flight.
+constexpr int kMergeThreads = 128;
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_head, int n_split,
+                                                              const float *__restrict__ ws,
+                                                              float *__restrict__ out) {
+    __shared__ float w_s[kMaxSplits];
+    __shared__ float red[kMergeThreads / 64];
     const int64_t rh = blockIdx.x;                    // row * n_head + head
     const int64_t RH = (int64_t)n_rows * n_head;
     const float *wm = ws;
     const float *wl = wm + (int64_t)n_split * RH;
     const float *wo = wl + (int64_t)n_split * RH;
-    float mstar = -INFINITY;
-    for (int i = 0; i < n_split; ++i) mstar = fmaxf(mstar, wm[i * RH + rh]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int tid = threadIdx.x;
+    float mloc = -INFINITY;
+    for (int i = tid; i < n_split; i += kMergeThreads) {
+        const float mi = wm[i * RH + rh];
+        w_s[i] = mi;
+        mloc = fmaxf(mloc, mi);
+    }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if ((tid & 63) == 0) red[tid >> 6] = mloc;
+    __syncthreads();
+    float mstar = red[0];
+#pragma unroll
+    for (int i = 1; i < kMergeThreads / 64; ++i) mstar = fmaxf(mstar, red[i]);
+    // weights 2^(m_i - m*) (0 for empty splits, and for every split if all are empty)
+    float lloc = 0.f;
+    for (int i = tid; i < n_split; i += kMergeThreads) {
+        const float mi = w_s[i];
+        const float wgt = (mstar == -INFINITY || mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - mstar);
+        w_s[i] = wgt;
+        if (wgt != 0.f) lloc += wgt * wl[i * RH + rh];
+    }
+    for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = lloc;
+    __syncthreads();
     float lsum = 0.f;
-    if (mstar != -INFINITY) {
-        for (int i = 0; i < n_split; ++i) {
-            const float mi = wm[i * RH + rh];
-            if (mi == -INFINITY) continue;
-            const float wgt = __builtin_amdgcn_exp2f(mi - mstar);
-            lsum += wgt * wl[i * RH + rh];
-            const f32x4 v = reinterpret_cast<const f32x4 *>(wo + (i * RH + rh) * kDV)[threadIdx.x];
-            acc += wgt * v;
+#pragma unroll
+    for (int i = 0; i < kMergeThreads / 64; ++i) lsum += red[i];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 *op = reinterpret_cast<const f32x4 *>(wo + rh * kDV) + tid;
+    const int64_t step4 = RH * kDV / 4;               // f32x4 stride between splits
+    int i = 0;
+    for (; i + 8 <= n_split; i += 8) {
+        f32x4 v[8];
+        float wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            wv[u] = w_s[i + u];
+            v[u] = wv[u] != 0.f ? op[(i + u) * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += wv[u] * v[u];
+    }
+    for (; i < n_split; ++i) {
+        const float wgt = w_s[i];
+        if (wgt != 0.f) acc += wgt * op[i * step4];
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    reinterpret_cast<f32x4 *>(out + rh * kDV)[threadIdx.x] = acc * inv;
+    reinterpret_cast<f32x4 *>(out + rh * kDV)[tid] = acc * inv;
 }
 
 template <int MB, int NW, int WK, int KIND, bool IDX>
@@ -634,7 +668,7 @@ hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream
 
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
                         hipStream_t stream) {
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)n_rows * n_head)), dim3(128), 0,
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)n_rows * n_head)), dim3(kMergeThreads), 0,
                        stream, n_rows, n_head, n_split, ws, out);
     return hipGetLastError();
 }
