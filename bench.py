@@ -42,7 +42,47 @@ def _args():
     ap.add_argument("--only", default="", help="run only these workloads, e.g. 'c2' or 'c3,c4'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
+                         "--copy-calibration into profiles/hbm_traffic.json and exit")
     return ap.parse_args()
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of the split-attention kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a 1 GiB device
+    copy (copy reads 1 GiB and writes 1 GiB)."""
+    out = {}
+    per = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
+        attn = [float(r["Counter_Value"]) for r in rows if "attn_kernel" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower()]
+        copy = [c for c in copy if c > 1e5]          # the 1 GiB copy, not small fills
+        if not attn or not copy:
+            raise SystemExit(f"{name}: no attention or copy dispatches in {d}")
+        factor = (1 << 30) / (max(copy) * 1024.0)    # bytes per counted KiB
+        per[name] = dict(kib_per_launch=float(np.median(attn)), copy_kib=max(copy), factor=factor,
+                         bytes_per_launch=float(np.median(attn)) * 1024.0 * factor)
+    out["decode_c2"] = dict(source_hash=_source_hash(),
+                            bytes_per_launch=per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"],
+                            read_bytes=per["FETCH_SIZE"]["bytes_per_launch"],
+                            write_bytes=per["WRITE_SIZE"]["bytes_per_launch"], counters=per)
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def _dev(a):
@@ -182,6 +222,9 @@ def _cpu_baseline(p, limit_s=40.0):
 
 def main():
     args = _args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is design-only in this build)", file=sys.stderr)

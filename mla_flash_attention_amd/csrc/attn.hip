@@ -117,7 +117,12 @@ __device__ __forceinline__ float shfl_f(float v, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
 
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70 & ~0xC00F); }
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched): gfx9 encoding, vmcnt in bits 3:0
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
 
 // ---------------------------------------------------------------------------------
 // The attention kernel.  NW waves, each owning MB blocks of 16 heads; WK waves share
@@ -130,9 +135,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     constexpr int kHS = NW / WK;                     // head sets per workgroup
     constexpr int kHPW = kHS * 16 * MB;              // heads per workgroup
     constexpr bool kQ8 = KIND == KV_Q8;
-    constexpr int kStageBytes = kTileBytes;
-    constexpr int kF16Stages = kQ8 ? 1 : 2;
-    constexpr int kLdsBytes = kF16Stages * kStageBytes + (kQ8 ? 2 * kQ8TileBytes : 0);
+    // A copy stage holds one tile's rows, then the tile's 64 f16 mask values, then the 64
+    // index-list entries of the tile after it.  LDS copies of 2-byte elements land in
+    // 4-byte slots (value zero-extended), so the mask area is 256 B as well.  16-bit
+    // caches copy straight into two such stages; Q8_0 copies raw rows into two stages
+    // and dequantises into one f16 tile.
+    constexpr int kRowArea = kQ8 ? kQ8TileBytes : kTileBytes;
+    constexpr int kMaskOff = kRowArea, kIdxOff = kRowArea + 256;
+    constexpr int kStageBytes = kRowArea + 256 + 256;
+    constexpr int kF16Off = 2 * kStageBytes;                       // Q8_0 only
+    constexpr int kLdsBytes = 2 * kStageBytes + (kQ8 ? kTileBytes : 0);
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     static_assert(WK == 1 || kHS * MB * (32 * 4 * 64 + 32) * 4 <= kLdsBytes, "key-half merge fits in LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
@@ -224,35 +236,34 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // upper 16 keys), columns 16*nb + 4*(j%4) .. +3 (byte 32*nb + 8*(j%4)).
     const int tr_off = (4 * g + (l16 >> 2)) * kLdsRow + 8 * (lane & 3);
 
-    // ---- prefetched side data.  idx_next: cache row of list position (tile start +
-    // lane) of the next tile to copy; mask_next / mask_cur: f16 mask bits of key (tile
-    // start + lane) of the tile in flight / being computed.
-    int idx_next = 0;
-    unsigned mask_cur = 0, mask_next = 0;
-    auto load_idx = [&](int it) __attribute__((always_inline)) {
-        if constexpr (IDX) {
-            int64_t pos = k0 + (int64_t)it * kTileKeys + lane;
-            if (pos >= k1) pos = k1 - 1;
-            idx_next = irow[pos];
-        }
-    };
+    // ---- first tile's index entries (later tiles' entries arrive by LDS copy)
+    int idx0 = 0;
+    if constexpr (IDX) {
+        int64_t pos = k0 + lane;
+        if (pos >= k1) pos = k1 - 1;
+        if (n_tiles > 0) idx0 = irow[pos];
+    }
 
-    // Copy tile `it` into stage `st` (HBM -> LDS; raw bytes for Q8_0), then prefetch
-    // the index entries of the tile after it.
-    auto issue_tile = [&](int it, unsigned char *__restrict__ dst) __attribute__((always_inline)) {
+    // Copy tile `it` into stage `dst` (HBM -> LDS; raw bytes for Q8_0) together with its
+    // mask values, and the index entries of tile `it + 1` after it.  Index entries of
+    // tile `it` come from `idx_src` (the previous stage's index area, or idx0 for the
+    // first tile).  Every copy is an LDS-DMA load: the loop holds no register results of
+    // global loads, so the only memory wait is the explicit one at the top of the loop.
+    auto issue_tile = [&](int it, unsigned char *__restrict__ dst, const unsigned char *__restrict__ idx_src)
+        __attribute__((always_inline)) {
         const int64_t kt = k0 + (int64_t)it * kTileKeys;
         const int last = (int)((k1 - kt) < kTileKeys ? (k1 - kt) : kTileKeys) - 1;  // last valid row
-        const int my_idx = idx_next;
-        if (mrow) {
-            const int r = lane < last ? lane : last;
-            const int64_t col = IDX ? (int64_t)my_idx : kt + r;
-            mask_next = mrow[IDX ? (int64_t)shfl_int(my_idx, r) : col];
-        }
-        const uint8_t *tbase = IDX ? kvs : kvs + kt * a.kv_row_stride;
-        // recompute the per-lane slot math each tile instead of keeping ~2 VGPRs per
-        // copy alive across the loop
         int ln = lane;
         asm volatile("" : "+v"(ln));
+        int my_idx = 0;                                    // cache row of list position kt + lane
+        if constexpr (IDX)
+            my_idx = it == 0 ? idx0 : reinterpret_cast<const int *>(idx_src + kIdxOff)[ln];
+        if (mrow) {
+            const int r = ln < last ? ln : last;
+            const int64_t col = IDX ? (int64_t)shfl_int(my_idx, r) : kt + r;
+            __builtin_amdgcn_global_load_lds((const void *)(mrow + col), (LDS_PTR(void))(dst + kMaskOff), 2, 0, 0);
+        }
+        const uint8_t *tbase = IDX ? kvs : kvs + kt * a.kv_row_stride;
         if constexpr (!kQ8) {
 #pragma unroll
             for (int j = 0; j < (kDmaPerTile + NW - 1) / NW; ++j) {
@@ -291,7 +302,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                 }
             }
         }
-        if (it + 1 < n_tiles) load_idx(it + 1);   // lands together with this tile
+        if constexpr (IDX) {                               // index entries of tile it + 1
+            int64_t pos = kt + kTileKeys + ln;
+            if (pos >= k1) pos = k1 - 1;
+            __builtin_amdgcn_global_load_lds((const void *)(irow + pos), (LDS_PTR(void))(dst + kIdxOff), 4, 0, 0);
+        }
     };
 
     // Dequantise a raw Q8_0 stage into the f16 tile (same swizzled layout).  One task
@@ -333,7 +348,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // LDS operands are loaded kQkD / kPvD steps ahead of the MFMAs that use them, and a
     // scheduling fence closes every step, so at most a few operands are in flight.
     constexpr int kQkD = 2, kPvD = 3;
-    auto compute_sub = [&](const unsigned char *stage, int64_t kt, int sub0) __attribute__((always_inline)) {
+    auto compute_sub = [&](const unsigned char *stage, const unsigned char *mask_lds, int64_t kt, int sub0)
+        __attribute__((always_inline)) {
         const unsigned char *sb = stage + sub0 * kLdsRow;
         // S^T = K . Q^T: A = 16 keys x 32 dims from LDS (two 16-key blocks), B = Q
         f32x4 sacc[2][MB];
@@ -363,15 +379,17 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         // i < 4: key sub0 + 4g + i; i >= 4: key sub0 + 16 + 4g + (i - 4)
         float bias[8];
         bool valid[8];
+        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};    // key k's mask: low half of dword k
+        if (mrow) {
+            const unsigned *mls = reinterpret_cast<const unsigned *>(mask_lds);
+            mk[0] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 4 * g);
+            mk[1] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 16 + 4 * g);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int kk = sub0 + 16 * (i >> 2) + 4 * g + (i & 3);
             valid[i] = kt + kk < k1;
-            bias[i] = 0.f;
-            if (mrow) {
-                const unsigned mb16 = (unsigned)shfl_int((int)mask_cur, kk) & 0xFFFFu;
-                bias[i] = f16_bits_to_f32((unsigned short)mb16) * kLog2e;
-            }
+            bias[i] = mrow ? f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e : 0.f;
         }
         u32x4 pa[MB];
 #pragma unroll
@@ -430,49 +448,48 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     };
 
     // One loop step: start copying tile `it + 1` into `next`, then compute tile `it`
-    // from `cur`.  The stage pointers are restrict-qualified: within a step the copy
-    // target and the tile being read never overlap, which lets the compiler keep the
-    // copy in flight across the LDS reads (without it, every LDS transpose read would
-    // wait for all outstanding copies).  Ordering between steps is explicit: wait for
-    // this wave's copies, then a barrier, at the top of every iteration.
-    auto step16 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur) __attribute__((always_inline)) {
-        if (it + 1 < n_tiles) issue_tile(it + 1, next);
+    // from `cur`.  The pointers are restrict-qualified: within a step the copy targets
+    // and the stage being read never overlap, which lets the compiler keep the copies
+    // in flight across the LDS reads (without it, every LDS transpose read would wait
+    // for all outstanding copies).  Ordering between steps is explicit: wait for this
+    // wave's copies, then a barrier, at the top of every iteration.
+    auto step16 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur)
+        __attribute__((always_inline)) {
+        if (it + 1 < n_tiles) issue_tile(it + 1, next, cur);
+        if (it < 0) return;
         const int64_t kt = k0 + (int64_t)it * kTileKeys;
 #pragma unroll 1
-        for (int sub = kp; sub < 2; sub += WK) compute_sub(cur, kt, sub * kSub);
+        for (int sub = kp; sub < 2; sub += WK) compute_sub(cur, cur + kMaskOff, kt, sub * kSub);
     };
-    auto stepq8 = [&](int it, unsigned char *__restrict__ next_raw, const unsigned char *__restrict__ raw,
+    auto stepq8 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur,
                       unsigned char *__restrict__ f16tile) __attribute__((always_inline)) {
-        if (it + 1 < n_tiles) issue_tile(it + 1, next_raw);
-        dequant_tile(raw, f16tile);
-        __syncthreads();
+        if (it + 1 < n_tiles) issue_tile(it + 1, next, cur);
+        if (it < 0) return;
+        dequant_tile(cur, f16tile);
+        // publish the f16 tile: this wave's LDS writes done, then a plain barrier (a full
+        // __syncthreads would also wait for the next tile's copy, which is still in flight)
+        __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0), vmcnt/expcnt untouched
+        __builtin_amdgcn_s_barrier();
         const int64_t kt = k0 + (int64_t)it * kTileKeys;
 #pragma unroll 1
-        for (int sub = kp; sub < 2; sub += WK) compute_sub(f16tile, kt, sub * kSub);
+        for (int sub = kp; sub < 2; sub += WK) compute_sub(f16tile, cur + kMaskOff, kt, sub * kSub);
     };
 
     // ---- main loop: one barrier per tile for 16-bit caches (it publishes tile `it`
     // and frees the other stage), two for Q8_0 (raw copy landed / f16 tile written).
-    if (n_tiles > 0) {
-        load_idx(0);
-        if constexpr (IDX) wait_vm0();
-        issue_tile(0, kQ8 ? lds + kStageBytes : lds);
-        for (int it = 0; it < n_tiles; ++it) {
+    // Iteration -1 only issues tile 0, so that every copy comes from the same inlined
+    // step (one set of alias scopes for the compiler to reason about).
+    for (int it = -1; it < n_tiles; ++it) {
+        if (it >= 0) {
             wait_vm0();
-            mask_cur = mask_next;
             __syncthreads();
-            // one inlined copy of the step with computed stage pointers (two copies
-            // selected by parity would double the register footprint)
-            if constexpr (kQ8) {
-                unsigned char *raw_next = lds + kStageBytes + ((it + 1) & 1) * kQ8TileBytes;
-                const unsigned char *raw_cur = lds + kStageBytes + (it & 1) * kQ8TileBytes;
-                stepq8(it, raw_next, raw_cur, lds);
-            } else {
-                unsigned char *next = lds + ((it + 1) & 1) * kStageBytes;
-                const unsigned char *cur = lds + (it & 1) * kStageBytes;
-                step16(it, next, cur);
-            }
         }
+        // one inlined copy of the step with computed stage pointers (two copies
+        // selected by parity would double the register footprint)
+        unsigned char *next = lds + ((it + 1) & 1) * kStageBytes;
+        const unsigned char *cur = lds + (it & 1) * kStageBytes;
+        if constexpr (kQ8) stepq8(it, next, cur, lds + kF16Off);
+        else step16(it, next, cur);
     }
 
 #pragma unroll
