@@ -17,9 +17,11 @@
 //
 // Design (gfx950-specific, not from the pages):
 //   * 64-key tiles of 576-wide rows are copied HBM -> LDS with global_load_lds_dwordx4
-//     (no VGPR staging), double-buffered, rows padded to a 1184-byte pitch so both LDS
-//     read patterns below are bank-conflict free.  Q8_0 tiles are DMA'd raw and
-//     dequantised LDS -> LDS to f16.
+//     (no VGPR staging), double-buffered.  A tile is stored as two areas: the 1024
+//     latent bytes of each row at a 1120-byte pitch, and the 128 RoPE bytes of each row
+//     packed 8 rows per KiB with an XOR swizzle.  Every copy then moves one contiguous
+//     KiB of LDS with all 64 lanes, and both LDS read patterns below are bank-conflict
+//     free.  Q8_0 tiles are DMA'd raw and dequantised LDS -> LDS to f16.
 //   * Q.K^T runs as S^T = K.Q^T on v_mfma_f32_16x16x32_{bf16,f16}: A = 16 keys from
 //     LDS, B = 16 heads of Q held in VGPRs for the whole kernel.  The accumulator
 //     layout (lane = head, 4 keys per lane) is exactly the A-operand layout P.V needs
@@ -45,15 +47,17 @@ typedef unsigned u32x2 __attribute__((__vector_size__(8)));
 #define LDS_PTR(T) __attribute__((address_space(3))) T *
 
 constexpr int kSub = 32;                                  // keys per compute sub-tile
-// An LDS tile row is the 1152-byte latent row plus 32 bytes of padding: with a 1184-byte
-// pitch (= 32 mod 256) both read patterns below are bank-conflict free on gfx950
-// (measured: 1152-byte pitch runs the S^T reads at ~1/4 and the transpose reads at ~1/3
-// of the padded rate).
-constexpr int kLdsRow = kRowBytes16 + 32;                 // 1184
-constexpr int kChunksPerLdsRow = kLdsRow / 16;            // 74 (72 data + 2 pad)
-constexpr int kTileBytes = kTileKeys * kLdsRow;           // 75,776
-constexpr int kDmaPerTile = kTileBytes / 1024;            // 74 wave-wide 1 KB copies
-static_assert(kTileBytes % 1024 == 0, "whole 1 KB copies per tile");
+// LDS tile layout.  Latent area: row r's bytes 0..1023 (dims 0..511, also V) at
+// r * kVRow.  The pitch 1120 (= 96 mod 256) keeps the S^T reads (16 rows, one 16-byte
+// column) and the transpose reads (4 rows x 32 bytes per 16 lanes) bank-conflict free
+// on gfx950 (measured: 1088 or 1072 halves both rates, and the unpadded 1152-byte row
+// quarters the S^T rate).  RoPE area: row r's bytes 1024..1151 (dims 512..575), 16-byte
+// chunk c stored at kRopeOff + 128 r + 16 (c ^ ((r >> 1) & 7)); 16 consecutive rows
+// reading one chunk then hit 16 distinct 16-byte bank groups.
+constexpr int kVRow = 1120;
+constexpr int kRopeOff = kTileKeys * kVRow;               // 71,680
+constexpr int kTileBytes = kRopeOff + kTileKeys * 128;    // 79,872
+__device__ __forceinline__ int rope_slot(int r, int c) { return 128 * r + 16 * (c ^ ((r >> 1) & 7)); }
 constexpr int kQ8TileBytes = kTileKeys * kQ8RowBytes;     // 39,168
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThresh = 8.0f;                    // log2 units
@@ -117,10 +121,11 @@ __device__ __forceinline__ float shfl_f(float v, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
 }
 
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched): gfx9 encoding, vmcnt in bits 3:0
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt untouched): gfx9 encoding, vmcnt bits 3:0 and
+// 15:14 (6 bits: at most 63 vector memory operations are counted per wave)
 template <int N> __device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 16, "vmcnt");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
 
@@ -146,6 +151,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     constexpr int kF16Off = 2 * kStageBytes;                       // Q8_0 only
     constexpr int kLdsBytes = 2 * kStageBytes + (kQ8 ? kTileBytes : 0);
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(kTileKeys % NW == 0 && 8 % NW == 0, "copy split over waves");
     static_assert(WK == 1 || kHS * MB * (32 * 4 * 64 + 32) * 4 <= kLdsBytes, "key-half merge fits in LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
 
@@ -230,11 +236,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     }
 
     // ---- per-lane LDS read offsets (relative to a sub-tile), tile-invariant
-    // S^T A operand: key row (kb*16 + l16), dims 32*s + 8*g .. +7 (byte 64*s + 16*g).
-    const int qk_off = l16 * kLdsRow + 16 * g;
+    // S^T A operand: key row (kb*16 + l16), dims 32*s + 8*g .. +7 (byte 64*s + 16*g);
+    // steps s = 16, 17 (RoPE dims) read chunk 4*(s-16) + g of the swizzled RoPE area
+    // (the swizzle depends on the row only through bits 1..3, which kb*16 and the
+    // sub-tile's 32-row offset leave unchanged).
+    const int qk_off = l16 * kVRow + 16 * g;
+    const int rope_off0 = rope_slot(l16, g), rope_off1 = rope_slot(l16, 4 + g);
     // P.V B operand via transpose read: lane 16G + j reads row 4G + j/4 (+16 for the
     // upper 16 keys), columns 16*nb + 4*(j%4) .. +3 (byte 32*nb + 8*(j%4)).
-    const int tr_off = (4 * g + (l16 >> 2)) * kLdsRow + 8 * (lane & 3);
+    const int tr_off = (4 * g + (l16 >> 2)) * kVRow + 8 * (lane & 3);
 
     // ---- first tile's index entries (later tiles' entries arrive by LDS copy)
     int idx0 = 0;
@@ -265,21 +275,37 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         }
         const uint8_t *tbase = IDX ? kvs : kvs + kt * a.kv_row_stride;
         if constexpr (!kQ8) {
+            // Latent copies: one per row, lane l moving bytes 16 l .. 16 l + 15 of the
+            // row; the row address is wave-uniform, so a copy costs scalar work only.
+            // RoPE copies: copy q fills the RoPE slots of rows 8q .. 8q + 7 (lane l: row
+            // 8q + l/8, slot l%8 holding chunk (l%8) ^ swizzle).  Rows past the range
+            // re-read the last valid row.
+            const int voff = ln * 16;
 #pragma unroll
-            for (int j = 0; j < (kDmaPerTile + NW - 1) / NW; ++j) {
-                const int blk = wave + j * NW;                 // 1 KB block of the stage
-                if (kDmaPerTile % NW != 0 && blk >= kDmaPerTile) break;
-                const int slot = blk * 64 + ln;                // 16-byte chunk slot
-                int r = slot / kChunksPerLdsRow;
-                int lc = slot - r * kChunksPerLdsRow;
-                lc = lc < 72 ? lc : lc - 2;                    // pad slots re-fetch chunks 70/71
-                r = r < last ? r : last;
+            for (int j = 0; j < kTileKeys / NW; ++j) {
+                const int r = wave + j * NW;                   // tile row (wave-uniform)
+                const int rc = r < last ? r : last;
+                const uint8_t *rowp;
+                if constexpr (IDX)
+                    rowp = tbase + (int64_t)__builtin_amdgcn_readlane(my_idx, rc) * a.kv_row_stride;
+                else
+                    rowp = tbase + (int64_t)rc * a.kv_row_stride;
+                __builtin_amdgcn_global_load_lds((const void *)(rowp + voff), (LDS_PTR(void))(dst + r * kVRow),
+                                                 16, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 8 / NW; ++j) {
+                const int q = wave + j * NW;
+                const int r = 8 * q + (ln >> 3);
+                const int rc = r < last ? r : last;
+                const int chunk = (ln & 7) ^ ((r >> 1) & 7);
                 const uint8_t *src;
                 if constexpr (IDX)
-                    src = tbase + (int64_t)shfl_int(my_idx, r) * a.kv_row_stride + lc * 16;
+                    src = tbase + (int64_t)shfl_int(my_idx, rc) * a.kv_row_stride;
                 else
-                    src = tbase + (uint32_t)(r * (uint32_t)a.kv_row_stride + lc * 16);
-                __builtin_amdgcn_global_load_lds((const void *)src, (LDS_PTR(void))(dst + blk * 1024), 16, 0, 0);
+                    src = tbase + (int64_t)rc * a.kv_row_stride;
+                __builtin_amdgcn_global_load_lds((const void *)(src + 1024 + 16 * chunk),
+                                                 (LDS_PTR(void))(dst + kRopeOff + q * 1024), 16, 0, 0);
             }
         } else {
             // raw Q8_0 rows of 612 bytes, packed back to back (153 dwords each)
@@ -309,7 +335,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         }
     };
 
-    // Dequantise a raw Q8_0 stage into the f16 tile (same swizzled layout).  One task
+    // Dequantise a raw Q8_0 stage into the f16 tile (the 16-bit tile layout).  One task
     // = one 34-byte block of one row: f16 scale d at byte 0, 32 int8 codes after it;
     // value = code * d, computed exactly in fp32 (8-bit code x 11-bit d) and rounded
     // once to f16.  Blocks are 2-byte aligned; 9 dwords cover one at either phase
@@ -337,9 +363,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     pk[2 * h] = pack_f16x2(fmaf((float)(u & 0xFFu), d, nd), fmaf((float)((u >> 8) & 0xFFu), d, nd));
                     pk[2 * h + 1] = pack_f16x2(fmaf((float)((u >> 16) & 0xFFu), d, nd), fmaf((float)(u >> 24), d, nd));
                 }
-                const int lc = 4 * b + c;
-                *reinterpret_cast<u32x4 *>(f16tile + r * kLdsRow + 16 * lc) =
-                    u32x4{pk[0], pk[1], pk[2], pk[3]};
+                const int lc = 4 * b + c;                                // 16-byte chunk of the row
+                unsigned char *dp = lc < 64 ? f16tile + r * kVRow + 16 * lc
+                                            : f16tile + kRopeOff + rope_slot(r, lc - 64);
+                *reinterpret_cast<u32x4 *>(dp) = u32x4{pk[0], pk[1], pk[2], pk[3]};
             }
         }
     };
@@ -350,7 +377,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     constexpr int kQkD = 2, kPvD = 3;
     auto compute_sub = [&](const unsigned char *stage, const unsigned char *mask_lds, int64_t kt, int sub0)
         __attribute__((always_inline)) {
-        const unsigned char *sb = stage + sub0 * kLdsRow;
+        const unsigned char *sb = stage + sub0 * kVRow;
+        const unsigned char *rb = stage + kRopeOff + sub0 * 128;
         // S^T = K . Q^T: A = 16 keys x 32 dims from LDS (two 16-key blocks), B = Q
         f32x4 sacc[2][MB];
 #pragma unroll
@@ -359,9 +387,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             for (int mb = 0; mb < MB; ++mb) sacc[kb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         u32x4 ka[kQkD + 1][2];
         auto load_k = [&](int s, u32x4 *dst) __attribute__((always_inline)) {
-            const int off = qk_off + 64 * s;
-            dst[0] = *reinterpret_cast<const u32x4 *>(sb + off);
-            dst[1] = *reinterpret_cast<const u32x4 *>(sb + off + 16 * kLdsRow);
+            if (s < 16) {
+                const int off = qk_off + 64 * s;
+                dst[0] = *reinterpret_cast<const u32x4 *>(sb + off);
+                dst[1] = *reinterpret_cast<const u32x4 *>(sb + off + 16 * kVRow);
+            } else {
+                const int off = s == 16 ? rope_off0 : rope_off1;
+                dst[0] = *reinterpret_cast<const u32x4 *>(rb + off);
+                dst[1] = *reinterpret_cast<const u32x4 *>(rb + off + 16 * 128);
+            }
         };
 #pragma unroll
         for (int s = 0; s < kQkD; ++s) load_k(s, ka[s]);
@@ -385,10 +419,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             mk[0] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 4 * g);
             mk[1] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 16 + 4 * g);
         }
+        // keys of this sub-tile still inside the range (>= 32 means all)
+        const int64_t rem64 = k1 - kt - sub0;
+        const int rem = rem64 < kSub ? (int)rem64 : kSub;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int kk = sub0 + 16 * (i >> 2) + 4 * g + (i & 3);
-            valid[i] = kt + kk < k1;
+            valid[i] = 16 * (i >> 2) + 4 * g + (i & 3) < rem;
             bias[i] = mrow ? f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e : 0.f;
         }
         u32x4 pa[MB];
@@ -432,7 +468,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         auto load_v = [&](int nb) __attribute__((always_inline)) -> u32x4 {
             const int off = tr_off + 32 * nb;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off + 16 * kLdsRow));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(sb + off + 16 * kVRow));
             const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
             return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         };
