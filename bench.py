@@ -166,7 +166,27 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0, split_phases=True):
     part_ms = [(e[1] if sparse else e[0]).elapsed_time(e[2]) for e in evs]
     merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
     kept = int(cnt.cpu()[0]) if sparse else None
-    return dict(total_ms=total_ms, step_ms=total_ms / steps, part_ms=float(np.mean(part_ms)),
+
+    # The step proper: the one-call API (attention then merge, back to back on the stream;
+    # compaction first on the sparse path) with no events between steps.
+    def call(i):
+        c = i % copies
+        if sparse:
+            B.fa_mask_compact(mask, idx, cnt, stream=stream)
+        B.mla_fa_decode(qs[c], p.q_type, kvs[c], p.kv_type, p.scale, out, mask=mask, kv_idx=idx,
+                        kv_idx_count=cnt, n_split=ns, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        call(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    call_ms = t_start.elapsed_time(t_end)
+    return dict(total_ms=call_ms, step_ms=call_ms / steps, evented_step_ms=total_ms / steps,
+                part_ms=float(np.mean(part_ms)),
                 part_ms_p10=float(np.percentile(part_ms, 10)), part_ms_p90=float(np.percentile(part_ms, 90)),
                 merge_ms=float(np.mean(merge_ms)),
                 compact_ms=None if compact_ms is None else float(np.mean(compact_ms)),

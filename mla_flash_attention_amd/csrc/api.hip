@@ -48,16 +48,19 @@ int env_splits() {
 }
 
 // Workgroup shape: heads per workgroup.  Split calls use 64-head workgroups whose two
-// key halves merge in LDS (half the partial bytes of 128-head workgroups); unsplit
-// calls use 128-head workgroups so each tile is read once per query row.
-int pick_shape(int n_head, int n_split) {
+// key halves merge in LDS (half the partial bytes of 128-head workgroups); unsplit calls
+// use 128-head workgroups so each tile is read once per query row.  The pair-kernel
+// shapes (p64, p128: half the LDS reads per MFMA, two exchanges per stage) are selected
+// only through the tuning override; measured on gfx950 they do not beat these.
+int pick_shape(int n_head, int n_split, int kv_type) {
     if (const char *e = std::getenv("MLA_FA_SHAPE")) {       // tuning only
-        switch (std::atoi(e)) {
-            case 16: return SHAPE_H16;
-            case 32: return SHAPE_H32;
-            case 64: return SHAPE_H64;
-            case 128: return SHAPE_H128;
-        }
+        const bool q8 = kv_type == MLA_FA_Q8_0;
+        if (!std::strcmp(e, "16")) return SHAPE_H16;
+        if (!std::strcmp(e, "32")) return SHAPE_H32;
+        if (!std::strcmp(e, "64")) return SHAPE_H64;
+        if (!std::strcmp(e, "128")) return SHAPE_H128;
+        if (!std::strcmp(e, "p64") && !q8) return SHAPE_P64;
+        if (!std::strcmp(e, "p128") && !q8) return SHAPE_P128;
     }
     if (n_head <= 16) return SHAPE_H16;
     if (n_head <= 32) return SHAPE_H32;
@@ -65,12 +68,13 @@ int pick_shape(int n_head, int n_split) {
     return SHAPE_H128;
 }
 
-int auto_splits(int64_t n_rows, int n_head, int64_t n_kv) {
+int auto_splits(int64_t n_rows, int n_head, int64_t n_kv, int kv_type) {
     const int env = env_splits();
     if (env) return env;
-    const int hg_split = (n_head + shape_heads(pick_shape(n_head, 2)) - 1) / shape_heads(pick_shape(n_head, 2));
-    if (n_rows * ((n_head + shape_heads(pick_shape(n_head, 1)) - 1) / shape_heads(pick_shape(n_head, 1))) >= kCUs)
-        return 1;
+    const int hs = shape_heads(pick_shape(n_head, 2, kv_type));
+    const int hu = shape_heads(pick_shape(n_head, 1, kv_type));
+    const int hg_split = (n_head + hs - 1) / hs;
+    if (n_rows * ((n_head + hu - 1) / hu) >= kCUs) return 1;
     int64_t s = (kCUs + n_rows * hg_split - 1) / (n_rows * hg_split);
     const int64_t max_by_len = (n_kv + kTileKeys * kMinTilesPerSplit - 1) / (kTileKeys * kMinTilesPerSplit);
     if (s > max_by_len) s = max_by_len;
@@ -87,10 +91,10 @@ struct Plan {
     int64_t split_chunk;
 };
 
-Plan make_plan(int64_t n_rows, int n_head, int64_t n_kv, int n_split) {
+Plan make_plan(int64_t n_rows, int n_head, int64_t n_kv, int kv_type, int n_split) {
     Plan p;
-    p.n_split = n_split > 0 ? n_split : auto_splits(n_rows, n_head, n_kv);
-    p.shape = pick_shape(n_head, p.n_split);
+    p.n_split = n_split > 0 ? n_split : auto_splits(n_rows, n_head, n_kv, kv_type);
+    p.shape = pick_shape(n_head, p.n_split, kv_type);
     const int hpw = shape_heads(p.shape);
     p.head_groups = (n_head + hpw - 1) / hpw;
     p.grid_x = p.head_groups > 1 ? 8 * p.head_groups * ((p.n_split + 7) / 8) : p.n_split;
@@ -232,15 +236,13 @@ const char *mla_fa_strerror(int status) {
 int mla_fa_version(void) { return 10000; }
 
 int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type) {
-    (void)kv_type;
     if (n_rows < 1 || n_kv < 1 || check_heads(n_head)) return 1;
-    return auto_splits(n_rows, n_head, n_kv);
+    return auto_splits(n_rows, n_head, n_kv, kv_type);
 }
 
 size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split) {
-    (void)kv_type;
     if (n_rows < 1 || n_kv < 1 || check_heads(n_head) || n_split < 0 || n_split > kMaxSplits) return 0;
-    Plan p = make_plan(n_rows, n_head, n_kv, n_split);
+    Plan p = make_plan(n_rows, n_head, n_kv, kv_type, n_split);
     return p.n_split > 1 ? partial_bytes(n_rows, n_head, p.n_split) : 0;
 }
 
@@ -255,7 +257,7 @@ int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_typ
                              n_split, workspace, workspace_bytes);
     int st = validate(c);
     if (st) return st;
-    Plan p = make_plan(n_seq, n_head, n_kv, n_split);
+    Plan p = make_plan(n_seq, n_head, n_kv, kv_type, n_split);
     return run_partials(c, p, static_cast<hipStream_t>(stream));
 }
 
@@ -279,7 +281,7 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
                              n_split, workspace, workspace_bytes);
     int st = validate(c);
     if (st) return st;
-    Plan p = make_plan(n_seq, n_head, n_kv, n_split);
+    Plan p = make_plan(n_seq, n_head, n_kv, kv_type, n_split);
     if (p.n_split > 1 && (!workspace || workspace_bytes < partial_bytes(n_seq, n_head, p.n_split)))
         return MLA_FA_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -301,7 +303,7 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
     c.scale = scale; c.out = out; c.n_split = n_split; c.ws = workspace; c.ws_bytes = workspace_bytes;
     int st = validate(c);
     if (st) return st;
-    Plan p = make_plan(n_tok, n_head, n_kv, n_split);
+    Plan p = make_plan(n_tok, n_head, n_kv, kv_type, n_split);
     if (p.n_split > 1 && (!workspace || workspace_bytes < partial_bytes(n_tok, n_head, p.n_split)))
         return MLA_FA_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);

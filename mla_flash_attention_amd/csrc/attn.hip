@@ -32,6 +32,8 @@
 //     the 512-wide O accumulators are rarely touched by the softmax.
 //   * A workgroup is NW waves = (NW/WK) head sets x WK key halves; key halves merge
 //     their (m, l, O) through LDS at the end, which halves split-KV partial traffic.
+#include <type_traits>
+
 #include "mla_fa_internal.h"
 
 namespace mlafa {
@@ -128,6 +130,16 @@ template <int N> __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vm0() { wait_vm<0>(); }
+
+// Workgroup barrier over LDS only: this wave's LDS operations complete, then s_barrier.
+// Outstanding global -> LDS copies are not waited for (a full __syncthreads would).
+// The empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------------
 // The attention kernel.  NW waves, each owning MB blocks of 16 heads; WK waves share
@@ -409,35 +421,33 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     sacc[kb][mb] = mfma16x16x32<KIND>(ka[s % (kQkD + 1)][kb], qreg[mb][s], sacc[kb][mb]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // mask bias (log2 units) and validity of this lane's 8 keys:
-        // i < 4: key sub0 + 4g + i; i >= 4: key sub0 + 16 + 4g + (i - 4)
-        float bias[8];
-        bool valid[8];
-        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};    // key k's mask: low half of dword k
-        if (mrow) {
-            const unsigned *mls = reinterpret_cast<const unsigned *>(mask_lds);
-            mk[0] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 4 * g);
-            mk[1] = *reinterpret_cast<const u32x4 *>(mls + sub0 + 16 + 4 * g);
-        }
-        // keys of this sub-tile still inside the range (>= 32 means all)
-        const int64_t rem64 = k1 - kt - sub0;
-        const int rem = rem64 < kSub ? (int)rem64 : kSub;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            valid[i] = 16 * (i >> 2) + 4 * g + (i & 3) < rem;
-            bias[i] = mrow ? f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e : 0.f;
-        }
+        // Scores in log2 units for this lane's 8 keys: i < 4: key sub0 + 4g + i; i >= 4: key
+        // sub0 + 16 + 4g + (i - 4).  The mask bias and the range check are applied only when
+        // present (uniform branches: most sub-tiles have neither).
+        const int64_t rem64 = k1 - kt - sub0;              // keys of this sub-tile in range
         u32x4 pa[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             float tv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tv[i] = sacc[i >> 2][mb][i & 3] * a.scale_log2;
+            if (mrow) {
+                const unsigned *mls = reinterpret_cast<const unsigned *>(mask_lds);
+                const u32x4 mk[2] = {*reinterpret_cast<const u32x4 *>(mls + sub0 + 4 * g),
+                                     *reinterpret_cast<const u32x4 *>(mls + sub0 + 16 + 4 * g)};
+#pragma unroll
+                for (int i = 0; i < 8; ++i)   // key k's mask: low half of dword k
+                    tv[i] += f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e;
+            }
+            if (rem64 < kSub) {
+                const int rem = (int)rem64;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (16 * (i >> 2) + 4 * g + (i & 3) >= rem) tv[i] = -INFINITY;
+            }
             float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float x = sacc[i >> 2][mb][i & 3] * a.scale_log2 + bias[i];
-                tv[i] = valid[i] ? x : -INFINITY;
-                mx = fmaxf(mx, tv[i]);
-            }
+            for (int i = 0; i < 8; ++i) mx = fmaxf(mx, tv[i]);
             mx = wave_max_groups(mx);
             const bool need = mx > m_run[mb] + kRescaleThresh;
             if (__builtin_amdgcn_ballot_w64(need)) {
@@ -618,27 +628,481 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// The pair kernel (16-bit caches).  A set of 32 heads is served by a pair of waves that
+// split the cache row between them: wave d = 0 scores dims 0..287 and accumulates dv
+// columns 0..255, wave d = 1 dims 288..575 and dv 256..511.  Every K or V byte a wave
+// reads from LDS then feeds 32 heads instead of 16, which halves LDS read traffic per
+// MFMA, while the wave still holds Q and O for only 32 x 288 and 32 x 256 values.  The
+// pair exchanges two things per stage through LDS: the partial scores of the partner's
+// 16 heads after Q.K^T, and the probabilities P of its own 16 heads after the online
+// softmax, which wave d runs for heads 16d .. 16d+15 of the set.
+//
+// Stages are 32 keys.  A 3-slot LDS ring holds stage n (scored in this iteration),
+// stage n-1 (its values accumulated in this iteration, so that the softmax of stage n
+// and P.V of stage n-1 are independent and can interleave) and stage n+1 (being
+// copied).  Two barriers per iteration: X publishes the copied stage and the previous
+// softmax results, Y publishes the partial scores.
+constexpr int kPK = 32;                                   // keys per stage
+constexpr int kPSlots = 3;
+constexpr int kPRopeOff = kPK * kVRow;                    // 35,840
+constexpr int kPMaskOff = kPRopeOff + kPK * 128;          // 39,936
+constexpr int kPIdxOff = kPMaskOff + 256;
+constexpr int kPStageBytes = kPIdxOff + 256;              // 40,448
+// Exchange area of one pair: partial scores [wave][kb][lane] 16 B, P [stage parity][wave]
+// [lane] 16 B, rescale factors [wave][16 heads], rescale flags [wave].
+constexpr int kXS = 0, kXP = 4096, kXA = 8192, kXF = 8320, kXBytes = 8448;
+
+template <int NP, int KIND, bool IDX>
+__global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
+    constexpr int NW = 2 * NP;
+    constexpr int kHPW = 32 * NP;
+    constexpr int kXOff = kPSlots * kPStageBytes;
+    constexpr int kLdsBytes = kXOff + NP * kXBytes;
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+    static_assert(kPK % NW == 0 && NW >= kPK / 8, "copy split over waves");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pr = wave >> 1;                         // head set of this wave
+    const int d = wave & 1;                           // half of the row (and softmax head block)
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+
+    int hg, split;
+    if (a.head_groups > 1) {
+        const int x = blockIdx.x;
+        hg = (x >> 3) % a.head_groups;
+        split = (x & 7) + 8 * (x / (8 * a.head_groups));
+    } else {
+        hg = 0;
+        split = blockIdx.x;
+    }
+    if (split >= a.n_split) return;
+    const int n_rows = a.n_seq * a.n_tok;
+    const int row_lin = (int)blockIdx.y;
+    const int s_idx = row_lin / a.n_tok;
+    const int t_idx = a.n_tok - 1 - row_lin % a.n_tok;
+    const int row = s_idx * a.n_tok + t_idx;
+    const uint8_t *kvs = a.kv + (int64_t)s_idx * a.kv_seq_stride;
+    const uint16_t *mrow = a.mask ? a.mask + (int64_t)s_idx * a.mask_seq_stride +
+                                        (int64_t)t_idx * a.mask_tok_stride
+                                  : nullptr;
+    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride : nullptr;
+    int64_t kend, chunk = a.split_chunk;
+    if constexpr (IDX) {
+        const int64_t c = a.kv_idx_count[s_idx];
+        kend = c < 0 ? 0 : (c > a.n_kv ? a.n_kv : c);
+        chunk = (kend + a.n_split - 1) / a.n_split;
+        chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+        if (chunk == 0) chunk = kTileKeys;
+    } else {
+        kend = a.causal ? a.n_kv - a.n_tok + t_idx + 1 : a.n_kv;
+    }
+    const int64_t k0 = (int64_t)split * chunk;
+    const int64_t k1 = k0 + chunk < kend ? k0 + chunk : kend;
+    const int n_st = k1 > k0 ? (int)((k1 - k0 + kPK - 1) / kPK) : 0;
+
+    // ---- Q: heads h_base + 16 hb + l16, k-steps 9d .. 9d+8 (dims 32 s + 8 g .. +7)
+    const int h_base = hg * kHPW + pr * 32;
+    u32x4 qreg[2][9];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const int head = h_base + hb * 16 + l16;
+        const bool ok = head < a.n_head;
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+            a.q + ((int64_t)row * a.n_head + (ok ? head : a.n_head - 1)) * kDK + 8 * g) + 4 * 9 * d;
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const u32x4 v = qp[4 * j];
+            qreg[hb][j] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // softmax state of heads 16 d + l16 (this wave's block); o[hb][nb]: heads 4g..4g+3 of
+    // block hb, dv column 256 d + 16 nb + l16
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[2][16];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) o[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // ---- LDS read offsets within a stage.  K-step j of this wave is s = 9 d + j; steps
+    // 0..15 are latent dims (byte 64 s + 16 g of the key row), 16 and 17 RoPE chunks.
+    // Step 8 of wave 1 reads RoPE chunk 4 + g = chunk (g ^ 4): its swizzled slot is that of
+    // step 7 with bit 6 of the byte offset flipped (stage bases and 128-byte rows keep
+    // bits 0..6 clear), so one offset register serves both steps.
+    const int qk_off = l16 * kVRow + 16 * g + 576 * d;
+    const int k7_lo = d ? kPRopeOff + rope_slot(l16, g) : qk_off + 448;
+    const int k_hi = d ? 16 * 128 : 16 * kVRow;       // second 16-key block, steps 7 and 8
+    const int tr_off = (4 * g + (l16 >> 2)) * kVRow + 8 * (lane & 3) + 512 * d;
+    unsigned char *xpair = lds + kXOff + pr * kXBytes;
+
+    int idx0 = 0;
+    if constexpr (IDX) {
+        int64_t pos = k0 + lane;
+        if (pos >= k1) pos = k1 - 1;
+        if (n_st > 0) idx0 = irow[pos];
+    }
+
+    // Copy stage n into `dst`: 32 latent rows (one full-wave copy each), the RoPE bytes of
+    // 8 rows per copy, the stage's mask values and the index entries of stage n + 1.  The
+    // copies are split into 7 parts of at most two instructions, which the copying waves
+    // issue one per Q.K^T step: issued all at once they would queue behind each other in
+    // the vector memory address unit (64 B per clock per CU) and stall the waves.  Four
+    // waves copy (all of them when NP = 2, group A when NP = 4).
+    constexpr int kNWC = 4;
+    static_assert(kPK % (2 * kNWC) == 0 && kPK / 8 == kNWC, "copy parts");
+    constexpr int kCopyParts = 7;
+    struct CopyPlan {
+        int64_t kt;
+        int last;
+        const uint8_t *tbase;
+        int my_idx;
+    };
+    auto copy_plan = [&](int n, const unsigned char *__restrict__ idx_src) __attribute__((always_inline)) {
+        CopyPlan c;
+        c.kt = k0 + (int64_t)n * kPK;
+        c.last = (int)((k1 - c.kt) < kPK ? (k1 - c.kt) : kPK) - 1;
+        c.my_idx = 0;
+        if constexpr (IDX) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            c.my_idx = n == 0 ? idx0 : reinterpret_cast<const int *>(idx_src + kPIdxOff)[ln];
+        }
+        c.tbase = IDX ? kvs : kvs + c.kt * a.kv_row_stride;
+        return c;
+    };
+    auto copy_part = [&](const CopyPlan &c, int part, unsigned char *__restrict__ dst) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (part < 4) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = wave + kNWC * (2 * part + e);
+                const int rc = r < c.last ? r : c.last;
+                const uint8_t *rowp;
+                if constexpr (IDX)
+                    rowp = c.tbase + (int64_t)__builtin_amdgcn_readlane(c.my_idx, rc) * a.kv_row_stride;
+                else
+                    rowp = c.tbase + (int64_t)rc * a.kv_row_stride;
+                __builtin_amdgcn_global_load_lds((const void *)(rowp + ln * 16), (LDS_PTR(void))(dst + r * kVRow), 16, 0, 0);
+            }
+        } else if (part == 4) {
+            const int q = wave;
+            const int r = 8 * q + (ln >> 3);
+            const int rc = r < c.last ? r : c.last;
+            const int chunk_i = (ln & 7) ^ ((r >> 1) & 7);
+            const uint8_t *src;
+            if constexpr (IDX)
+                src = c.tbase + (int64_t)shfl_int(c.my_idx, rc) * a.kv_row_stride;
+            else
+                src = c.tbase + (int64_t)rc * a.kv_row_stride;
+            __builtin_amdgcn_global_load_lds((const void *)(src + 1024 + 16 * chunk_i),
+                                             (LDS_PTR(void))(dst + kPRopeOff + q * 1024), 16, 0, 0);
+        } else if (part == 5) {
+            if (mrow && wave == kNWC - 1) {
+                const int r = ln < c.last ? ln : c.last;
+                const int64_t col = IDX ? (int64_t)shfl_int(c.my_idx, r) : c.kt + r;
+                __builtin_amdgcn_global_load_lds((const void *)(mrow + col), (LDS_PTR(void))(dst + kPMaskOff), 2, 0, 0);
+            }
+        } else if (part == 6) {
+            if constexpr (IDX) {
+                if (wave == kNWC - 2) {
+                    int64_t pos = c.kt + kPK + ln;
+                    if (pos >= k1) pos = k1 - 1;
+                    __builtin_amdgcn_global_load_lds((const void *)(irow + pos), (LDS_PTR(void))(dst + kPIdxOff), 4, 0, 0);
+                }
+            }
+        }
+    };
+
+    constexpr int kQkD = 1, kPvD = 3;             // operand ring depths (register budget)
+    // Two schedules, one barrier-phase apart.  X (top of iteration n) publishes the copied
+    // stage n; Y (mid-iteration) publishes partial scores, P and rescale factors.
+    //   group A: [X] Q.K^T(n)                 [Y] softmax(n), P.V(n - 1)
+    //   group B: [X] softmax(n - 1)           [Y] Q.K^T(n), P.V(n - 1)
+    // With 8 waves, pairs 0-1 run A and pairs 2-3 run B; wave w and w + 4 share a SIMD, so
+    // each SIMD has one wave in an MFMA phase while the other runs its softmax.  Both
+    // groups read only stages n and n - 1 in iteration n, so the third slot can receive
+    // stage n + 1.  P is double-buffered by stage parity; scores and factors are
+    // single-buffered (each is read in the phase after it is written, before the next write).
+    const bool grp_b = NP == 4 && pr >= 2;
+
+    // Rescale both head blocks by the factors the owners published with P of the last
+    // softmax (before that stage's P.V accumulates into O).
+    auto rescale = [&](const unsigned char *__restrict__ xch) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const unsigned flag = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const unsigned *>(xch + kXF + 16 * hb));
+            if (flag) {
+                const f32x4 al = *reinterpret_cast<const f32x4 *>(xch + kXA + 64 * hb + 16 * g);
+#pragma unroll
+                for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[hb][nb][r] *= al[r];
+            }
+        }
+    };
+    // Partial scores of this wave's dims for both head blocks of stage `st`; the partner's
+    // block goes to LDS, this wave's own block is returned.
+    auto qk = [&](const unsigned char *__restrict__ st, unsigned char *__restrict__ xch, f32x4 *own,
+                  auto &&on_step) __attribute__((always_inline)) {
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) sacc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 ka[kQkD + 1][2];
+        auto load_k = [&](int j, u32x4 *dstk) __attribute__((always_inline)) {
+            int lo, hi;
+            if (j < 7) { lo = qk_off + 64 * j; hi = lo + 16 * kVRow; }
+            else if (j == 7) { lo = k7_lo; hi = k7_lo + k_hi; }
+            else { lo = d ? (k7_lo ^ 64) : k7_lo + 64; hi = lo + k_hi; }
+            dstk[0] = *reinterpret_cast<const u32x4 *>(st + lo);
+            dstk[1] = *reinterpret_cast<const u32x4 *>(st + hi);
+        };
+#pragma unroll
+        for (int j = 0; j < kQkD; ++j) load_k(j, ka[j]);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            if (j + kQkD < 9) load_k(j + kQkD, ka[(j + kQkD) % (kQkD + 1)]);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    sacc[kb][hb] = mfma16x16x32<KIND>(ka[j % (kQkD + 1)][kb], qreg[hb][j], sacc[kb][hb]);
+            on_step(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            *reinterpret_cast<f32x4 *>(xch + kXS + d * 2048 + kb * 1024 + 16 * lane) = d ? sacc[kb][0] : sacc[kb][1];
+            own[kb] = d ? sacc[kb][1] : sacc[kb][0];
+        }
+    };
+    // Online softmax of stage m for this wave's head block: full scores = own partial +
+    // the partner's; publishes P(m) (parity m & 1), the rescale factors and the flag.
+    auto softmax = [&](int m, const f32x4 *own, const unsigned char *__restrict__ st,
+                       unsigned char *__restrict__ xch) __attribute__((always_inline)) {
+        const int64_t kt = k0 + (int64_t)m * kPK;
+        f32x4 oth[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            oth[kb] = *reinterpret_cast<const f32x4 *>(xch + kXS + (1 - d) * 2048 + kb * 1024 + 16 * lane);
+        u32x4 mk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        if (mrow) {
+            const unsigned *mls = reinterpret_cast<const unsigned *>(st + kPMaskOff);
+            mk[0] = *reinterpret_cast<const u32x4 *>(mls + 4 * g);
+            mk[1] = *reinterpret_cast<const u32x4 *>(mls + 16 + 4 * g);
+        }
+        const int64_t rem64 = k1 - kt;
+        const int rem = rem64 < kPK ? (int)rem64 : kPK;
+        // scores of this lane: i < 4 key 4g + i, i >= 4 key 16 + 4g + (i - 4)
+        float tv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float sc = own[i >> 2][i & 3] + oth[i >> 2][i & 3];
+            const float bias = mrow ? f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e : 0.f;
+            const float x = sc * a.scale_log2 + bias;
+            tv[i] = 16 * (i >> 2) + 4 * g + (i & 3) < rem ? x : -INFINITY;
+            mx = fmaxf(mx, tv[i]);
+        }
+        mx = wave_max_groups(mx);
+        const bool need = mx > m_run + kRescaleThresh;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(need);
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        m_run = need ? mx : m_run;
+        l_run *= alpha;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float pv[8], ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(tv[i] - m_use);
+            ps += pv[i];
+        }
+        l_run += ps;
+        // every lane writes its head's factor (lanes with equal l16 agree)
+        reinterpret_cast<float *>(xch + kXA + 64 * d)[l16] = alpha;
+        *reinterpret_cast<unsigned *>(xch + kXF + 16 * d) = bal != 0ull ? 1u : 0u;
+        *reinterpret_cast<u32x4 *>(xch + kXP + (m & 1) * 2048 + d * 1024 + 16 * lane) =
+            u32x4{pack_p<KIND>(pv[0], pv[1]), pack_p<KIND>(pv[2], pv[3]),
+                  pack_p<KIND>(pv[4], pv[5]), pack_p<KIND>(pv[6], pv[7])};
+    };
+    // O += P(m) . V(m) for this wave's dv half, V from stage `st`.
+    auto pv = [&](int m, const unsigned char *__restrict__ st, const unsigned char *__restrict__ xch)
+        __attribute__((always_inline)) {
+        const unsigned char *xpp = xch + kXP + (m & 1) * 2048 + 16 * lane;
+        const u32x4 pa[2] = {*reinterpret_cast<const u32x4 *>(xpp), *reinterpret_cast<const u32x4 *>(xpp + 1024)};
+        auto load_v = [&](int nb) __attribute__((always_inline)) -> u32x4 {
+            const int off = tr_off + 32 * nb;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(st + off));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(st + off + 16 * kVRow));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+        u32x4 vb[kPvD + 1];
+#pragma unroll
+        for (int nb = 0; nb < kPvD; ++nb) vb[nb] = load_v(nb);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+            if (nb + kPvD < 16) vb[(nb + kPvD) % (kPvD + 1)] = load_v(nb + kPvD);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) o[hb][nb] = mfma16x16x32<KIND>(pa[hb], vb[nb % (kPvD + 1)], o[hb][nb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // own-block partial scores of the last Q.K^T, carried from phase Y to the next X (group B)
+    f32x4 keep[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // One iteration.  Restrict-qualified stage pointers: the copy target never overlaps the
+    // stages or the exchange area read in the same iteration (without it the compiler
+    // would make every LDS read wait for the copies in flight).
+    auto step = [&](auto GB_, int n, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur,
+                    const unsigned char *__restrict__ prev, unsigned char *__restrict__ xch)
+        __attribute__((always_inline)) {
+        constexpr bool GB = decltype(GB_)::value;
+        if constexpr (!GB) {
+            if (n >= 1) rescale(xch);
+            f32x4 own[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            // n + 1 < n_st implies n < n_st: the copy of stage n + 1 rides on this Q.K^T
+            if (n + 1 < n_st) {
+                const CopyPlan cp = copy_plan(n + 1, cur);
+                qk(cur, xch, own, [&](int j) __attribute__((always_inline)) {
+                    if (j < kCopyParts) copy_part(cp, j, next);
+                });
+            } else if (n < n_st) {
+                qk(cur, xch, own, [](int) {});
+            }
+            lds_barrier();                                   // Y
+            if (n < n_st) softmax(n, own, cur, xch);
+            __builtin_amdgcn_sched_barrier(0);
+            if (n >= 1) pv(n - 1, prev, xch);
+        } else {
+            if (n >= 1) softmax(n - 1, keep, prev, xch);
+            lds_barrier();                                   // Y
+            if (n >= 1) rescale(xch);
+            if (n < n_st) qk(cur, xch, keep, [](int) {});
+            __builtin_amdgcn_sched_barrier(0);
+            if (n >= 1) pv(n - 1, prev, xch);
+        }
+    };
+
+    // one loop per schedule (a single loop holding both would hold both live sets)
+    auto run = [&](auto GB_) __attribute__((always_inline)) {
+        // the prologue copies stage 0 (copying waves only)
+        if (wave < kNWC) {
+            const CopyPlan cp = copy_plan(0, lds);
+#pragma unroll
+            for (int part = 0; part < kCopyParts; ++part) copy_part(cp, part, lds);
+        }
+        // ring slots rotate (prev, cur, next) -> (cur, next, prev) every iteration
+        unsigned char *cur = lds, *next = lds + kPStageBytes, *prev = lds + 2 * kPStageBytes;
+        for (int n = 0; n <= n_st; ++n) {
+            wait_vm0();
+            __syncthreads();                         // X: stage n landed
+            step(GB_, n, next, cur, prev, xpair);
+            unsigned char *t = prev;
+            prev = cur;
+            cur = next;
+            next = t;
+        }
+    };
+    if (n_st > 0) {
+        if (grp_b) run(std::true_type{});
+        else run(std::false_type{});
+    }
+
+    // ---- epilogue: l of both head blocks, then the output or this split's partial
+    l_run = wave_sum_groups(l_run);
+    __syncthreads();
+    float *xl = reinterpret_cast<float *>(xpair + kXA);     // [wave][16] = l of block d
+    if (lane < 16) xl[16 * d + lane] = l_run;
+    __syncthreads();
+    if (a.n_split == 1) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(xl + 16 * hb + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ir = l4[r] > 0.f ? 1.f / l4[r] : 0.f;
+                const int head = h_base + hb * 16 + 4 * g + r;
+                if (head < a.n_head) {
+                    float *op = a.out + ((int64_t)row * a.n_head + head) * kDV + 256 * d + l16;
+#pragma unroll
+                    for (int nb = 0; nb < 16; ++nb) op[16 * nb] = o[hb][nb][r] * ir;
+                }
+            }
+        }
+    } else {
+        const int64_t RH = (int64_t)n_rows * a.n_head;
+        float *wm = a.ws;
+        float *wl = wm + (int64_t)a.n_split * RH;
+        float *wo = wl + (int64_t)a.n_split * RH;
+        const int64_t base = (int64_t)split * RH + (int64_t)row * a.n_head;
+        const int head_l = h_base + 16 * d + l16;
+        if (lane < 16 && head_l < a.n_head) {
+            wm[base + head_l] = m_run;
+            wl[base + head_l] = l_run;
+        }
+        if (n_st > 0) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int head = h_base + hb * 16 + 4 * g + r;
+                    if (head < a.n_head) {
+                        float *op = wo + (base + head) * kDV + 256 * d + l16;
+#pragma unroll
+                        for (int nb = 0; nb < 16; ++nb) op[16 * nb] = o[hb][nb][r];
+                    }
+                }
+        }
+    }
+}
+
 // Merge split partials: out = sum_i 2^(m_i - m*) O_i / sum_i 2^(m_i - m*) l_i; splits with
-// m_i = -inf (no kept key) weigh 0 and their O_i is never read; a row with no kept key
-// anywhere outputs 0.  One workgroup per (row, head): the per-split (m, l) are loaded
-// in parallel into LDS, then each thread streams its 4 dv columns of every split's O
-// with several independent loads in flight.
-constexpr int kMergeThreads = 128;
+// m_i = -inf (no kept key) weigh 0 and their O_i never contributes (it may be unwritten);
+// a row with no kept key anywhere outputs 0.  One workgroup per (row, head); thread t owns
+// dv quad t % 128 of splits t / 128, t / 128 + 4, ...  The partial O reads are the whole
+// cost, so they start first: each thread issues its first 8 loads, then (m_i, l_i) of all
+// splits are read in one round trip, reduced to the weights in LDS, and the loads already
+// in flight are weighted (a select drops unweighted splits); later batches follow, and
+// the four split groups are summed through LDS.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeGroups = kMergeThreads / 128;
+constexpr int kMergeBatch = 8;
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_head, int n_split,
                                                               const float *__restrict__ ws,
                                                               float *__restrict__ out) {
     __shared__ float w_s[kMaxSplits];
+    __shared__ float l_s[kMaxSplits];
     __shared__ float red[kMergeThreads / 64];
+    __shared__ f32x4 part[kMergeGroups - 1][128];
     const int64_t rh = blockIdx.x;                    // row * n_head + head
     const int64_t RH = (int64_t)n_rows * n_head;
     const float *wm = ws;
     const float *wl = wm + (int64_t)n_split * RH;
     const float *wo = wl + (int64_t)n_split * RH;
     const int tid = threadIdx.x;
+    const int q = tid & 127, sg = tid >> 7;
+    const f32x4 *op = reinterpret_cast<const f32x4 *>(wo + rh * kDV) + q;
+    const int64_t step4 = RH * kDV / 4;               // f32x4 stride between splits
+
+    f32x4 v0[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+        const int i = sg + u * kMergeGroups;
+        v0[u] = i < n_split ? op[(int64_t)i * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     float mloc = -INFINITY;
     for (int i = tid; i < n_split; i += kMergeThreads) {
         const float mi = wm[i * RH + rh];
         w_s[i] = mi;
+        l_s[i] = wl[i * RH + rh];
         mloc = fmaxf(mloc, mi);
     }
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
@@ -653,7 +1117,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
         const float mi = w_s[i];
         const float wgt = (mstar == -INFINITY || mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - mstar);
         w_s[i] = wgt;
-        if (wgt != 0.f) lloc += wgt * wl[i * RH + rh];
+        if (wgt != 0.f) lloc += wgt * l_s[i];
     }
     for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off);
     __syncthreads();
@@ -662,33 +1126,51 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < kMergeThreads / 64; ++i) lsum += red[i];
+
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const f32x4 *op = reinterpret_cast<const f32x4 *>(wo + rh * kDV) + tid;
-    const int64_t step4 = RH * kDV / 4;               // f32x4 stride between splits
-    int i = 0;
-    for (; i + 8 <= n_split; i += 8) {
-        f32x4 v[8];
-        float wv[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            wv[u] = w_s[i + u];
-            v[u] = wv[u] != 0.f ? op[(i + u) * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kMergeBatch; ++u) {
+        const int i = sg + u * kMergeGroups;
+        const float wgt = i < n_split ? w_s[i] : 0.f;
+        if (wgt != 0.f) acc += wgt * v0[u];
+    }
+    int i = sg + kMergeBatch * kMergeGroups;
+    for (; i + (kMergeBatch - 1) * kMergeGroups < n_split; i += kMergeBatch * kMergeGroups) {
+        f32x4 v[kMergeBatch];
+        float wv[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            wv[u] = w_s[i + u * kMergeGroups];
+            v[u] = wv[u] != 0.f ? op[(int64_t)(i + u * kMergeGroups) * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wv[u] * v[u];
+        for (int u = 0; u < kMergeBatch; ++u) acc += wv[u] * v[u];
     }
-    for (; i < n_split; ++i) {
+    for (; i < n_split; i += kMergeGroups) {
         const float wgt = w_s[i];
-        if (wgt != 0.f) acc += wgt * op[i * step4];
+        if (wgt != 0.f) acc += wgt * op[(int64_t)i * step4];
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    reinterpret_cast<f32x4 *>(out + rh * kDV)[tid] = acc * inv;
+    if (sg > 0) part[sg - 1][q] = acc;
+    __syncthreads();
+    if (sg == 0) {
+#pragma unroll
+        for (int k = 0; k < kMergeGroups - 1; ++k) acc += part[k][q];
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        reinterpret_cast<f32x4 *>(out + rh * kDV)[q] = acc * inv;
+    }
 }
 
 template <int MB, int NW, int WK, int KIND, bool IDX>
 hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     dim3 grid(a.grid_x, a.n_seq * a.n_tok);
     hipLaunchKernelGGL((attn_kernel<MB, NW, WK, KIND, IDX>), grid, dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int NP, int KIND, bool IDX>
+hipError_t launch_pair(const AttnArgs &a, hipStream_t stream) {
+    dim3 grid(a.grid_x, a.n_seq * a.n_tok);
+    hipLaunchKernelGGL((attn_pair_kernel<NP, KIND, IDX>), grid, dim3(NP * 128), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -699,6 +1181,14 @@ hipError_t launch_shape(const AttnArgs &a, int shape, hipStream_t stream) {
         case SHAPE_H32: return launch_one<1, 4, 2, KIND, IDX>(a, stream);
         case SHAPE_H64: return launch_one<1, 8, 2, KIND, IDX>(a, stream);
         case SHAPE_H128: return launch_one<1, 8, 1, KIND, IDX>(a, stream);
+        // pair shapes: dense 16-bit caches only; Q8_0 and indexed rows run the single-wave
+        // kernel with the same heads per workgroup (so the plan's head groups still hold)
+        case SHAPE_P64:
+            if constexpr (KIND != KV_Q8 && !IDX) return launch_pair<2, KIND, IDX>(a, stream);
+            return launch_one<1, 8, 2, KIND, IDX>(a, stream);
+        case SHAPE_P128:
+            if constexpr (KIND != KV_Q8 && !IDX) return launch_pair<4, KIND, IDX>(a, stream);
+            return launch_one<1, 8, 1, KIND, IDX>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -15,10 +15,10 @@ constexpr int kMaxSplits = 1024;
 
 enum KvKind { KV_BF16 = 0, KV_F16 = 1, KV_Q8 = 2 };
 
-// Workgroup shapes: MB 16-head blocks per wave, NW waves, WK waves sharing one head
-// set and splitting each tile's keys between them.  Heads per workgroup =
-// (NW / WK) * 16 * MB.
-enum Shape { SHAPE_H16 = 0, SHAPE_H32 = 1, SHAPE_H64 = 2, SHAPE_H128 = 3 };
+// Workgroup shapes.  H*: MB 16-head blocks per wave, NW waves, WK waves sharing one
+// head set and splitting each tile's keys between them; heads per workgroup =
+// (NW / WK) * 16 * MB.  P*: pair kernel (16-bit caches only), 32 heads per wave pair.
+enum Shape { SHAPE_H16 = 0, SHAPE_H32 = 1, SHAPE_H64 = 2, SHAPE_H128 = 3, SHAPE_P64 = 4, SHAPE_P128 = 5 };
 
 struct AttnArgs {
     const uint16_t *q;             // [n_seq][n_tok][n_head][576]
@@ -58,6 +58,12 @@ hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_r
                           hipStream_t stream);
 
 // Heads per workgroup of each shape.
-inline int shape_heads(int shape) { return 16 << shape; }
+inline int shape_heads(int shape) {
+    switch (shape) {
+        case SHAPE_P64: return 64;
+        case SHAPE_P128: return 128;
+    }
+    return 16 << shape;
+}
 
 }  // namespace mlafa
