@@ -211,27 +211,55 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     const int64_t k1 = k0 + chunk < kend ? k0 + chunk : kend;
     const int n_tiles = k1 > k0 ? (int)((k1 - k0 + kTileKeys - 1) / kTileKeys) : 0;
 
-    // ---- Q of this wave's heads, resident in VGPRs: B operand of S^T = K.Q^T
+    // ---- Q of this wave's heads, resident in VGPRs: B operand of S^T = K.Q^T.  With two
+    // key-half waves per head set (WK = 2) both need the same Q: the workgroup copies its
+    // heads' Q rows once into LDS (the area the second tile lands in later; for Q8_0 the
+    // f16 tile) and each wave reads its rows at the first iteration.  Otherwise each wave
+    // loads its rows directly.
     const int h_base = hg * kHPW + hs * 16 * MB;
+    constexpr bool kQviaLds = WK == 2 && MB == 1 && !kQ8;   // (Q8_0: the extra live range spills)
+    constexpr int kQOff = kQ8 ? kF16Off : kStageBytes;
+    static_assert(!kQviaLds || (kHPW * kRowBytes16 <= (kQ8 ? kTileBytes : kStageBytes) &&
+                                (kHPW * kRowBytes16) % (1024 * NW) == 0), "Q staging area");
     u32x4 qreg[MB][18];
+    auto q_fix = [&](u32x4 v, bool ok) __attribute__((always_inline)) {
+        if (!ok) v = u32x4{0, 0, 0, 0};
+        if constexpr (kQ8) {
+            if (a.q_bf16) {   // bf16 -> f16 for the f16 MFMA
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int head = h_base + mb * 16 + l16;
-        const bool ok = head < a.n_head;
-        const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-            a.q + ((int64_t)row * a.n_head + (ok ? head : a.n_head - 1)) * kDK + 8 * g);
-#pragma unroll
-        for (int s = 0; s < 18; ++s) {
-            u32x4 v = qp[4 * s];
-            if (!ok) v = u32x4{0, 0, 0, 0};
-            if constexpr (kQ8) {
-                if (a.q_bf16) {   // bf16 -> f16 for the f16 MFMA
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = pack_f16x2(bf16_bits_to_f32(v[e] & 0xFFFFu), bf16_bits_to_f32(v[e] >> 16));
-                }
+                for (int e = 0; e < 4; ++e)
+                    v[e] = pack_f16x2(bf16_bits_to_f32(v[e] & 0xFFFFu), bf16_bits_to_f32(v[e] >> 16));
             }
-            qreg[mb][s] = v;
+        }
+        return v;
+    };
+    if constexpr (kQviaLds) {
+        if (n_tiles > 0) {
+            // rows of heads hg*kHPW .. +kHPW-1, contiguous in Q; absent heads re-read the last
+            // row (and are zeroed when read back)
+            const int h0 = hg * kHPW;
+            const int nh = a.n_head - h0 < kHPW ? a.n_head - h0 : kHPW;
+            const uint8_t *qb = reinterpret_cast<const uint8_t *>(a.q + ((int64_t)row * a.n_head + h0) * kDK);
+#pragma unroll
+            for (int j = 0; j < kHPW * kRowBytes16 / (1024 * NW); ++j) {
+                const int chunk = wave + j * NW;
+                const int o = chunk * 1024 + lane * 16;
+                int hl = o / kRowBytes16;
+                const int inrow = o - hl * kRowBytes16;
+                hl = hl < nh ? hl : nh - 1;
+                __builtin_amdgcn_global_load_lds((const void *)(qb + hl * kRowBytes16 + inrow),
+                                                 (LDS_PTR(void))(lds + kQOff + chunk * 1024), 16, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int head = h_base + mb * 16 + l16;
+            const bool ok = head < a.n_head;
+            const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+                a.q + ((int64_t)row * a.n_head + (ok ? head : a.n_head - 1)) * kDK + 8 * g);
+#pragma unroll
+            for (int s = 0; s < 18; ++s) qreg[mb][s] = q_fix(qp[4 * s], ok);
         }
     }
 
@@ -529,6 +557,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         if (it >= 0) {
             wait_vm0();
             __syncthreads();
+        }
+        if constexpr (kQviaLds) {
+            if (it == 0) {   // Q landed with tile 0: read this wave's rows before tile 1 overwrites them
+                const int hl = hs * 16 + l16;
+                const bool ok = h_base + l16 < a.n_head;
+                const unsigned char *qr = lds + kQOff + hl * kRowBytes16 + 16 * g;
+#pragma unroll
+                for (int s = 0; s < 18; ++s) qreg[0][s] = q_fix(*reinterpret_cast<const u32x4 *>(qr + 64 * s), ok);
+                lds_barrier();
+            }
         }
         // one inlined copy of the step with computed stage pointers (two copies
         // selected by parity would double the register footprint)
