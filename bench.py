@@ -113,8 +113,12 @@ def _traffic(kernel_key):
     return e.get("bytes_per_launch")
 
 
-def _time_decode(B, p, copies, steps, warmup, n_split=0, split_phases=True):
-    """Per-step split-attention and merge durations (events on the launch stream)."""
+def _time_decode(B, p, copies, steps, warmup, n_split=0):
+    """Per-call times on the launch stream.  step: the one-call API (compaction first on the
+    sparse path, then attention and merge) repeated back to back between two events;
+    kernel, merge and compaction: that launch alone repeated back to back (what a
+    kernel-trace profiler averages).  Inputs rotate over `copies` distinct copies.  The
+    p10/p90 spread of the attention kernel comes from events around single launches."""
     import torch
     from mla_flash_attention_amd import synth
     stream = torch.cuda.current_stream()
@@ -131,66 +135,55 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0, split_phases=True):
     if sparse:
         idx = torch.empty((p.n_seq, p.n_kv), dtype=torch.int32, device="cuda")
         cnt = torch.empty((p.n_seq,), dtype=torch.int32, device="cuda")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
 
-    def step(i, ev=None):
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def compact(i):
+        B.fa_mask_compact(mask, idx, cnt, stream=stream)
+
+    def part(i):
         c = i % copies
-        if ev is not None:
-            ev[0].record(stream)
-        if sparse:
-            B.fa_mask_compact(mask, idx, cnt, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-        B.mla_fa_decode_partials(qs[c], p.q_type, kvs[c], p.kv_type, p.scale, out, mask=mask,
-                                 kv_idx=idx, kv_idx_count=cnt, n_split=ns, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        if ns > 1:
-            B.mla_fa_merge_partials(p.n_seq, p.n_head, ns, out, ws, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+        B.mla_fa_decode_partials(qs[c], p.q_type, kvs[c], p.kv_type, p.scale, out, mask=mask, kv_idx=idx,
+                                 kv_idx_count=cnt, n_split=ns, workspace=ws, stream=stream)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(steps):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    compact_ms = [e[0].elapsed_time(e[1]) for e in evs] if sparse else None
-    part_ms = [(e[1] if sparse else e[0]).elapsed_time(e[2]) for e in evs]
-    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    kept = int(cnt.cpu()[0]) if sparse else None
+    def merge(i):
+        B.mla_fa_merge_partials(p.n_seq, p.n_head, ns, out, ws, stream=stream)
 
-    # The step proper: the one-call API (attention then merge, back to back on the stream;
-    # compaction first on the sparse path) with no events between steps.
     def call(i):
-        c = i % copies
         if sparse:
-            B.fa_mask_compact(mask, idx, cnt, stream=stream)
+            compact(i)
+        c = i % copies
         B.mla_fa_decode(qs[c], p.q_type, kvs[c], p.kv_type, p.scale, out, mask=mask, kv_idx=idx,
                         kv_idx_count=cnt, n_split=ns, workspace=ws, stream=stream)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    t_start.record(stream)
+    compact_ms = timed(compact) if sparse else None
+    part_ms = timed(part)
+    merge_ms = timed(merge) if ns > 1 else 0.0
+    step_ms = timed(call)
+    single = []
     for i in range(steps):
-        call(i)
-    t_end.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        part(i)
+        e1.record(stream)
+        single.append((e0, e1))
     torch.cuda.synchronize()
-    call_ms = t_start.elapsed_time(t_end)
-    return dict(total_ms=call_ms, step_ms=call_ms / steps, evented_step_ms=total_ms / steps,
-                part_ms=float(np.mean(part_ms)),
-                part_ms_p10=float(np.percentile(part_ms, 10)), part_ms_p90=float(np.percentile(part_ms, 90)),
-                merge_ms=float(np.mean(merge_ms)),
-                compact_ms=None if compact_ms is None else float(np.mean(compact_ms)),
-                n_split=ns, kept=kept)
+    single_ms = [a.elapsed_time(b) for a, b in single]
+    kept = int(cnt.cpu()[0]) if sparse else None
+    return dict(total_ms=step_ms * steps, step_ms=step_ms, part_ms=part_ms,
+                part_ms_p10=float(np.percentile(single_ms, 10)), part_ms_p90=float(np.percentile(single_ms, 90)),
+                merge_ms=merge_ms, compact_ms=compact_ms, n_split=ns, kept=kept)
 
 
 def _time_prefill(B, p, steps, warmup):
