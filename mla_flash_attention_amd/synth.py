@@ -136,6 +136,10 @@ class Problem:
     scale: np.float32
     causal: bool = False
     mask: np.ndarray | None = None
+    kv_len: np.ndarray | None = None      # int32 [n_seq] valid cells per sequence
+    alibi: np.ndarray | None = None       # float32 [n_head] per-head mask slopes
+    sinks: np.ndarray | None = None       # float32 [n_head] per-head sink logits
+    softcap: float = 0.0                  # 0 = off
 
     @property
     def shared_kv(self) -> bool:
@@ -170,10 +174,15 @@ def make_problem(kind: str = "decode", n_seq: int = 1, n_tok: int = 1, n_head: i
                  n_kv: int = 1024, q_type: int = TYPE_BF16, kv_type: int = TYPE_BF16,
                  seed: int = 0, causal: bool = False, sparse: bool = False,
                  mask_kind: str | None = None, q_gain: float = 1.0,
-                 scale: float | None = None, name: str = "", dk: int = DK) -> Problem:
+                 scale: float | None = None, name: str = "", dk: int = DK,
+                 ragged: bool = False, alibi: bool = False, sinks: bool = False,
+                 softcap: float = 0.0) -> Problem:
     """Draw one problem.  `mask_kind`: None, "runs" (sparse runs of kept cells),
     "runs_bias" (runs with finite random biases on kept cells), "random" (iid 50%
-    kept with finite biases), "none_kept" (every cell -inf)."""
+    kept with finite biases), "none_kept" (every cell -inf), "distance" (minus the
+    distance |pos_t - j| of each cell to the query position, as ALiBi masks carry).
+    ragged: valid cells per sequence drawn from U{n_tok..n_kv} (stream 3); alibi:
+    per-head slopes 2^(-8(h+1)/n_head); sinks: per-head sink logits 2*N(0,1) (stream 4)."""
     gq, gk, gm = rng(seed, 0), rng(seed, 1), rng(seed, 2)
     qf = gq.standard_normal((n_seq, n_tok, n_head, dk), dtype=np.float32)
     if q_gain != 1.0:
@@ -184,12 +193,30 @@ def make_problem(kind: str = "decode", n_seq: int = 1, n_tok: int = 1, n_head: i
     kv = quantize_q8_0(kf) if kv_type == TYPE_Q8_0 else round_bits(kf, kv_type)
     if (sparse or kind == "sparse") and mask_kind is None:
         mask_kind = "runs"
-    mask = make_mask(mask_kind, n_seq, n_tok, n_kv, gm)
+    kv_len = None
+    if ragged:
+        kv_len = rng(seed, 3).integers(n_tok, n_kv + 1, n_seq).astype(np.int32)
+    if mask_kind == "distance":
+        mask = np.empty((n_seq, n_tok, n_kv), dtype=np.uint16)
+        for s_ in range(n_seq):
+            length = n_kv if kv_len is None else int(kv_len[s_])
+            for t in range(n_tok):
+                pos = length - n_tok + t
+                mask[s_, t] = f32_to_f16_bits(-np.abs(pos - np.arange(n_kv, dtype=np.float32)))
+    else:
+        mask = make_mask(mask_kind, n_seq, n_tok, n_kv, gm)
+    slopes = None
+    if alibi:
+        slopes = np.exp2(-8.0 * (np.arange(n_head, dtype=np.float64) + 1) / n_head).astype(np.float32)
+    sink = None
+    if sinks:
+        sink = (2.0 * rng(seed, 4).standard_normal(n_head)).astype(np.float32)
     return Problem(name=name or f"{kind} s{n_seq} t{n_tok} h{n_head} kv{n_kv}", kind=kind,
                    q=q_bits, q_type=q_type, kv=kv, kv_type=kv_type, n_seq=n_seq,
                    n_tok=n_tok, n_head=n_head, n_kv=n_kv,
                    scale=np.float32(DEFAULT_SCALE if scale is None else scale),
-                   causal=causal, mask=mask)
+                   causal=causal, mask=mask, kv_len=kv_len, alibi=slopes, sinks=sink,
+                   softcap=float(np.float32(softcap)))
 
 
 def make_mask(mask_kind: str | None, n_seq: int, n_tok: int, n_kv: int,

@@ -40,6 +40,14 @@ def _lib():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_mla_attention_ext.restype = ctypes.c_int64
+        lib.oracle_mla_attention_ext.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+            ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p]
         lib.oracle_mask_compact.restype = None
         lib.oracle_mask_compact.argtypes = [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
@@ -77,13 +85,16 @@ def decode_q8_0_rows(rows: np.ndarray, dk: int) -> np.ndarray:
 
 
 def attention(q, q_type, kv, kv_type, n_seq, n_tok, n_head, n_kv, scale, *, causal=False,
-              mask=None, rows=None, dk=576, dv=512, kv_shared=False, return_stats=False):
+              mask=None, rows=None, dk=576, dv=512, kv_shared=False, return_stats=False,
+              kv_len=None, alibi=None, sinks=None, softcap=0.0):
     """fp64 attention outputs [len(rows) or n_seq*n_tok*n_head][dv].
 
     q: uint16 [n_seq][n_tok][n_head][dk]; kv: [n_seq or 1][n_kv][row] (uint16 rows of
     dk elements, or uint8 Q8_0 rows); mask: uint16 [n_seq][n_tok][n_kv] or None;
     scale: the fp32 value passed to the GPU (widened here); rows: flat row ids
-    (s*n_tok + t)*n_head + h.
+    (s*n_tok + t)*n_head + h.  kv_len: int [n_seq] valid cells per sequence (None = all
+    n_kv); alibi / sinks: float [n_head] slopes / sink logits (the fp32 values passed to
+    the GPU, widened); softcap: 0 = off.
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     kv = np.ascontiguousarray(kv)
@@ -98,26 +109,36 @@ def attention(q, q_type, kv, kv_type, n_seq, n_tok, n_head, n_kv, scale, *, caus
         n_rows = rows.size
     else:
         n_rows = n_seq * n_tok * n_head
+    if kv_len is not None:
+        kv_len = np.ascontiguousarray(kv_len, dtype=np.int32).reshape(n_seq)
+    if alibi is not None:
+        alibi = np.ascontiguousarray(np.asarray(alibi, dtype=np.float32), dtype=np.float64).reshape(n_head)
+    if sinks is not None:
+        sinks = np.ascontiguousarray(np.asarray(sinks, dtype=np.float32), dtype=np.float64).reshape(n_head)
     out = np.zeros((n_rows, dv), dtype=np.float64)
     rmax = np.zeros(n_rows, dtype=np.float64)
     rsum = np.zeros(n_rows, dtype=np.float64)
-    rc = _lib().oracle_mla_attention(
+    rc = _lib().oracle_mla_attention_ext(
         _ptr(q), q_type, _ptr(kv), kv_type, row_bytes, seq_stride, n_seq, n_tok, n_head,
-        n_kv, dk, dv, 1 if causal else 0, _ptr(mask), n_kv, n_tok * n_kv,
-        float(np.float32(scale)), _ptr(rows), n_rows, _ptr(out), _ptr(rmax), _ptr(rsum))
+        n_kv, dk, dv, _ptr(kv_len), 1 if causal else 0, _ptr(mask), n_kv, n_tok * n_kv,
+        _ptr(alibi), _ptr(sinks), float(np.float32(softcap)), float(np.float32(scale)),
+        _ptr(rows), n_rows, _ptr(out), _ptr(rmax), _ptr(rsum))
     if rc < 0:
-        raise ValueError(f"oracle_mla_attention failed ({rc})")
+        raise ValueError(f"oracle_mla_attention_ext failed ({rc})")
     if return_stats:
         return out, rmax, rsum
     return out
 
 
 def attention_problem(p, rows=None, return_stats=False):
-    """Oracle outputs for a synthetic problem object (duck-typed: q, kv, mask, ...)."""
+    """Oracle outputs for a synthetic problem object (duck-typed: q, kv, mask, ...;
+    optional kv_len, alibi, sinks, softcap)."""
     return attention(p.q, p.q_type, p.kv, p.kv_type, p.n_seq, p.n_tok, p.n_head, p.n_kv,
                      p.scale, causal=p.causal, mask=p.mask, rows=rows,
                      dk=p.q.shape[-1], dv=512 if p.q.shape[-1] == 576 else p.q.shape[-1],
-                     return_stats=return_stats)
+                     return_stats=return_stats, kv_len=getattr(p, "kv_len", None),
+                     alibi=getattr(p, "alibi", None), sinks=getattr(p, "sinks", None),
+                     softcap=getattr(p, "softcap", 0.0))
 
 
 def mask_compact(mask2d: np.ndarray):

@@ -128,21 +128,33 @@ int oracle_num_threads(void) {
  *   q    : bits [n_seq][n_tok][n_head][dk], f16 or bf16
  *   kv   : row j of sequence s starts at kv + s*kv_seq_stride + j*kv_row_stride
  *          (bytes; kv_seq_stride 0 = all sequences share one cache)
+ *   kv_len : valid cells per sequence (clamped to [0, n_kv]), or NULL = n_kv for all
+ *   causal : token t of sequence s sees cells j <= L_s - n_tok + t (L_s its valid length)
  *   mask : f16 bits, element (s, t, j) at s*mask_seq_stride + t*mask_tok_stride + j,
- *          or NULL
+ *          or NULL; -inf (bits 0xFC00) drops the cell, any other value is an additive
+ *          bias on the scaled score
+ *   alibi : per-head slope, or NULL; with it the bias of a kept cell is slope * mask
+ *          value (a dropped cell stays dropped)
+ *   sinks : per-head sink logit, or NULL; it joins the softmax normaliser as one more
+ *          term exp(sink - m) that carries no value
+ *   softcap : 0 = off; else the scaled score x becomes softcap * tanh(x / softcap),
+ *          before the bias is added
  *   rows : flat row ids to evaluate (NULL = all n_seq*n_tok*n_head, in order)
- *   row_max / row_sum : optional, the max score m and sum of exp(score - m) per
- *          row (m = -inf and sum 0 for a row with no kept key)
- * Returns the number of rows with no kept key, or a negative value on bad input.
+ *   row_max / row_sum : optional, per row the max m over kept scores and the sink, and
+ *          the normaliser sum of exp(score - m) (+ exp(sink - m)); m = -inf and sum 0
+ *          for a row with neither kept cell nor sink
+ * Returns the number of rows with no kept cell, or a negative value on bad input.
  */
-int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, int kv_type,
-                             int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
-                             int n_tok, int n_head, int64_t n_kv, int dk, int dv, int causal,
-                             const uint16_t *mask, int64_t mask_tok_stride,
-                             int64_t mask_seq_stride, double scale, const int64_t *rows,
-                             int64_t n_rows, double *out, double *row_max, double *row_sum) {
+int64_t oracle_mla_attention_ext(const uint16_t *q, int q_type, const uint8_t *kv, int kv_type,
+                                 int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                                 int n_tok, int n_head, int64_t n_kv, int dk, int dv,
+                                 const int32_t *kv_len, int causal, const uint16_t *mask,
+                                 int64_t mask_tok_stride, int64_t mask_seq_stride,
+                                 const double *alibi, const double *sinks, double softcap,
+                                 double scale, const int64_t *rows, int64_t n_rows, double *out,
+                                 double *row_max, double *row_sum) {
     if (!q || !kv || !out || n_seq < 1 || n_tok < 1 || n_head < 1 || n_kv < 1 || dk < 1 ||
-        dv < 1 || dv > dk)
+        dv < 1 || dv > dk || softcap < 0.0)
         return -1;
     if (q_type != OR_F16 && q_type != OR_BF16) return -1;
     if (kv_type == OR_Q8_0 && dk % 32) return -1;
@@ -158,13 +170,15 @@ int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, i
             wanted = (r / ((int64_t)n_tok * n_head)) == s;
         }
         if (!wanted) continue;
+        int64_t len = n_kv;
+        if (kv_len) len = kv_len[s] < 0 ? 0 : (kv_len[s] > n_kv ? n_kv : kv_len[s]);
 
-        /* The sequence's whole cache, decoded once to fp64. */
-        double *K = (double *)malloc((size_t)n_kv * dk * sizeof(double));
+        /* The sequence's valid cells, decoded once to fp64. */
+        double *K = (double *)malloc((size_t)(len > 0 ? len : 1) * dk * sizeof(double));
         if (!K) return -3;
         const uint8_t *kv_s = kv + (int64_t)s * kv_seq_stride;
 #pragma omp parallel for schedule(static)
-        for (int64_t j = 0; j < n_kv; ++j)
+        for (int64_t j = 0; j < len; ++j)
             decode_row(kv_s + j * kv_row_stride, kv_type, dk, K + j * dk);
 
 #pragma omp parallel for schedule(dynamic, 1) reduction(+ : n_empty)
@@ -172,47 +186,55 @@ int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, i
             int64_t r = rows ? rows[i] : i;
             if (r / ((int64_t)n_tok * n_head) != s) continue;
             int t = (int)((r / n_head) % n_tok);
+            int h = (int)(r % n_head);
             double *qv = (double *)malloc((size_t)dk * sizeof(double));
-            double *score = (double *)malloc((size_t)n_kv * sizeof(double));
-            double *p = (double *)malloc((size_t)n_kv * sizeof(double));
+            double *score = (double *)malloc((size_t)(len > 0 ? len : 1) * sizeof(double));
+            double *p = (double *)malloc((size_t)(len > 0 ? len : 1) * sizeof(double));
             double *o = out + i * dv;
             decode_row((const uint8_t *)(q + r * dk), q_type, dk, qv);
 
-            /* score_j = scale * q.k_j + mask_j, or -inf for a key that is not kept */
+            /* score_j = cap(scale * q.k_j) + bias_j, or -inf for a cell that is not kept */
             double m = -INFINITY;
-            for (int64_t j = 0; j < n_kv; ++j) {
+            int kept = 0;
+            for (int64_t j = 0; j < len; ++j) {
                 double bias = 0.0;
                 if (mask) {
                     uint16_t mb = mask[(int64_t)s * mask_seq_stride + (int64_t)t * mask_tok_stride + j];
                     bias = oracle_f16_to_f64(mb);
+                    if (alibi && bias != -INFINITY) bias = alibi[h] * bias;
                 }
-                if (causal && j > n_kv - n_tok + t) bias = -INFINITY;
+                if (causal && j > len - n_tok + t) bias = -INFINITY;
                 if (bias == -INFINITY) {
                     score[j] = -INFINITY;
                     continue;
                 }
                 double dot = 0.0;
                 for (int d = 0; d < dk; ++d) dot += qv[d] * K[j * dk + d];
-                score[j] = scale * dot + bias;
+                double x = scale * dot;
+                if (softcap > 0.0) x = softcap * tanh(x / softcap);
+                score[j] = x + bias;
+                kept = 1;
                 if (score[j] > m) m = score[j];
             }
+            const double sink = sinks ? sinks[h] : -INFINITY;
+            if (sink > m) m = sink;
 
             for (int d = 0; d < dv; ++d) o[d] = 0.0;
+            if (!kept) n_empty += 1;
             if (m == -INFINITY) {
-                /* no kept key: output zeros */
+                /* neither a kept cell nor a sink: output zeros */
                 if (row_max) row_max[i] = -INFINITY;
                 if (row_sum) row_sum[i] = 0.0;
-                n_empty += 1;
             } else {
-                /* softmax weights, materialised in full */
-                double l = 0.0;
-                for (int64_t j = 0; j < n_kv; ++j) {
+                /* softmax weights, materialised in full; the sink adds to the normaliser */
+                double l = sink == -INFINITY ? 0.0 : exp(sink - m);
+                for (int64_t j = 0; j < len; ++j) {
                     p[j] = score[j] == -INFINITY ? 0.0 : exp(score[j] - m);
                     l += p[j];
                 }
-                for (int64_t j = 0; j < n_kv; ++j) p[j] /= l;
+                for (int64_t j = 0; j < len; ++j) p[j] /= l;
                 /* weighted sum of V = the first dv columns of each row */
-                for (int64_t j = 0; j < n_kv; ++j) {
+                for (int64_t j = 0; j < len; ++j) {
                     if (p[j] == 0.0) continue;
                     const double *v = K + j * dk;
                     for (int d = 0; d < dv; ++d) o[d] += p[j] * v[d];
@@ -227,6 +249,19 @@ int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, i
         free(K);
     }
     return n_empty;
+}
+
+/* The plain call: every sequence holds n_kv cells; no ALiBi, sinks or softcap. */
+int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, int kv_type,
+                             int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                             int n_tok, int n_head, int64_t n_kv, int dk, int dv, int causal,
+                             const uint16_t *mask, int64_t mask_tok_stride,
+                             int64_t mask_seq_stride, double scale, const int64_t *rows,
+                             int64_t n_rows, double *out, double *row_max, double *row_sum) {
+    return oracle_mla_attention_ext(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_tok,
+                                    n_head, n_kv, dk, dv, NULL, causal, mask, mask_tok_stride,
+                                    mask_seq_stride, NULL, NULL, 0.0, scale, rows, n_rows, out,
+                                    row_max, row_sum);
 }
 
 /* Sparse-mask index compaction: for each mask row, the ascending list of cells
