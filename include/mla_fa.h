@@ -142,6 +142,41 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Batched attention over per-sequence caches of different lengths, with the logit
+ * softcap, ALiBi slopes and attention sinks that the Metal tensor-API flash-attention
+ * kernel supports for the 576/512 shape ("llama.cpp Metal: tensor-API flash attention
+ * for F16 KV caches" news item; the pages name the features, the readings below are
+ * the plain ones).  mla_fa_decode is the special case n_tok = 1, kv_len = NULL,
+ * causal = 0 and no extras (less the sparse index path, which only it offers).
+ *   q        [n_seq][n_tok][n_head][576] f16/bf16 bits (device).
+ *   kv       row j of sequence s at kv + s*kv_seq_stride + j*kv_row_stride (bytes);
+ *            n_kv rows of capacity per sequence; alignment as for decode.
+ *   kv_len   NULL (every sequence holds n_kv cells), or int32 [n_seq] (device): the
+ *            valid cells of each sequence, clamped to [0, n_kv].
+ *   causal   nonzero: token t of sequence s attends to cells j <= L_s - n_tok + t (L_s
+ *            its valid length; a row left with no cell outputs 0).  Without kv_len it
+ *            requires n_tok <= n_kv.
+ *   mask     NULL, or f16 bits, element (s, t, j) at s*mask_seq_stride +
+ *            t*mask_tok_stride + j: -inf drops the cell, other values add to the score.
+ *   alibi_slopes NULL, or fp32 [n_head] (device): the bias of a kept cell for head h is
+ *            alibi_slopes[h] times its mask value (dropped cells stay dropped).
+ *   sinks    NULL, or fp32 [n_head] (device): a per-head logit that joins the softmax
+ *            normaliser as one more term exp(sinks[h] - m) carrying no value.
+ *   softcap  0 = off; > 0: the scaled score x = scale * q.k becomes
+ *            softcap * tanh(x / softcap) before the mask bias is added.
+ *   out      [n_seq][n_tok][n_head][512] fp32 (device).
+ *   n_split / workspace as for decode with n_rows = n_seq * n_tok.
+ * Errors: as for decode; ERR_INVALID also for a negative or non-finite softcap and for
+ * kv_len / alibi_slopes / sinks not 4-byte aligned.
+ */
+int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                  int64_t kv_seq_stride, int n_seq, int n_tok, int n_head, int64_t n_kv,
+                  const int32_t *kv_len, int causal, const uint16_t *mask, int64_t mask_seq_stride,
+                  int64_t mask_tok_stride, const float *alibi_slopes, const float *sinks, float softcap,
+                  float scale, float *out, int n_split, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
  * Sparse-mask index compaction.  For each of n_rows f16 mask rows (row r at
  * mask + r*mask_row_stride elements, n_kv cells), writes the ascending list of cells
  * whose mask is not -inf (bit pattern != 0xFC00) to idx + r*idx_row_stride and its

@@ -22,7 +22,7 @@ MLA_FA_OK, MLA_FA_ERR_INVALID, MLA_FA_ERR_UNSUPPORTED, MLA_FA_ERR_WORKSPACE, MLA
 
 EXPORTS = ("mla_fa_strerror", "mla_fa_version", "mla_fa_auto_splits", "mla_fa_workspace_size",
            "mla_fa_decode", "mla_fa_decode_partials", "mla_fa_merge_partials", "mla_fa_prefill",
-           "fa_mask_compact")
+           "mla_fa_attend", "fa_mask_compact")
 
 _LIB = None
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.mla_fa_prefill.argtypes = [_p, _i, _p, _i, _i64, _i, _i, _i64, _i, _p, _i64, _f, _p, _i, _p, _sz, _p]
         L.fa_mask_compact.restype = _i
         L.fa_mask_compact.argtypes = [_p, _i64, _i, _i64, _p, _i64, _p, _p]
+        L.mla_fa_attend.restype = _i
+        L.mla_fa_attend.argtypes = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64, _i64,
+                                    _p, _p, _f, _f, _p, _i, _p, _sz, _p]
         _LIB = L
     return _LIB
 
@@ -87,6 +90,11 @@ def _row_stride_bytes(kv: torch.Tensor) -> int:
     return kv.stride(-2) * kv.element_size()
 
 
+def _seq_stride_bytes(kv: torch.Tensor, n_seq: int) -> int:
+    """Bytes between sequences' caches; 0 when one cache serves every sequence."""
+    return kv.stride(0) * kv.element_size() if kv.dim() == 3 and kv.shape[0] > 1 else 0
+
+
 def mla_fa_version() -> int:
     return int(lib().mla_fa_version())
 
@@ -109,7 +117,7 @@ def _decode_args(q, q_type, kv, kv_type, scale, out, mask, kv_idx, kv_idx_count,
                  workspace, stream):
     n_seq, n_head = q.shape[0], q.shape[-2]
     n_kv = kv.shape[-2]
-    kv_seq_stride = kv.stride(0) * kv.element_size() if kv.dim() == 3 and kv.shape[0] > 1 else 0
+    kv_seq_stride = _seq_stride_bytes(kv, n_seq)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (_ptr(q), q_type, _ptr(kv), kv_type, _row_stride_bytes(kv), kv_seq_stride, n_seq, n_head,
             n_kv, _ptr(mask), 0 if mask is None else mask.stride(0), _ptr(kv_idx), _ptr(kv_idx_count),
@@ -153,6 +161,25 @@ def mla_fa_prefill(q, q_type, kv, kv_type, scale, out, *, causal=True, mask=None
                                 0 if mask is None else mask.stride(-2), float(scale), _ptr(out),
                                 n_split, _ptr(workspace), ws_bytes, _stream(stream)),
            "mla_fa_prefill")
+    return out
+
+
+def mla_fa_attend(q, q_type, kv, kv_type, scale, out, *, kv_len=None, causal=False, mask=None,
+                  alibi=None, sinks=None, softcap=0.0, n_split=0, workspace=None, stream=None):
+    """q [n_seq][n_tok][n_head][576], kv [n_seq][n_kv][row] (n_kv = capacity), out fp32
+    [n_seq][n_tok][n_head][512]; kv_len int32 [n_seq]; mask [n_seq][n_tok][>=n_kv] f16
+    bits; alibi / sinks fp32 [n_head]; softcap 0 = off."""
+    n_seq, n_tok, n_head = q.shape[0], q.shape[1], q.shape[2]
+    n_kv = kv.shape[-2]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    mseq = 0 if mask is None else mask.stride(0)
+    mtok = 0 if mask is None else mask.stride(1)
+    _check(lib().mla_fa_attend(_ptr(q), q_type, _ptr(kv), kv_type, _row_stride_bytes(kv),
+                               _seq_stride_bytes(kv, n_seq), n_seq, n_tok, n_head, n_kv, _ptr(kv_len),
+                               1 if causal else 0, _ptr(mask), mseq, mtok, _ptr(alibi), _ptr(sinks),
+                               float(softcap), float(scale), _ptr(out), n_split, _ptr(workspace), ws_bytes,
+                               _stream(stream)),
+           "mla_fa_attend")
     return out
 
 

@@ -121,6 +121,10 @@ struct Common {
     int n_split;
     void *ws;
     size_t ws_bytes;
+    const int32_t *kv_len = nullptr;
+    const float *alibi = nullptr;
+    const float *sinks = nullptr;
+    float softcap = 0.f;
 };
 
 int validate(const Common &c) {
@@ -138,13 +142,15 @@ int validate(const Common &c) {
     if (!aligned(c.kv, kva) || c.kv_row_stride < row_bytes(c.kv_type) || c.kv_row_stride % kva ||
         c.kv_seq_stride < 0 || c.kv_seq_stride % kva)
         return MLA_FA_ERR_INVALID;
-    if (c.causal && c.n_tok > c.n_kv) return MLA_FA_ERR_INVALID;
+    if (c.causal && !c.kv_len && c.n_tok > c.n_kv) return MLA_FA_ERR_INVALID;
     if (c.mask) {
         if (!aligned(c.mask, 2) || c.mask_seq_stride < 0 || c.mask_tok_stride < 0)
             return MLA_FA_ERR_INVALID;
         if (c.n_seq > 1 && c.mask_seq_stride < c.n_kv) return MLA_FA_ERR_INVALID;
         if (c.n_tok > 1 && c.mask_tok_stride < c.n_kv) return MLA_FA_ERR_INVALID;
     }
+    if (!(c.softcap >= 0.f) || !std::isfinite(c.softcap)) return MLA_FA_ERR_INVALID;
+    if (!aligned(c.kv_len, 4) || !aligned(c.alibi, 4) || !aligned(c.sinks, 4)) return MLA_FA_ERR_INVALID;
     if ((c.kv_idx == nullptr) != (c.kv_idx_count == nullptr)) return MLA_FA_ERR_INVALID;
     if (c.kv_idx) {
         if (c.n_tok != 1 || c.causal) return MLA_FA_ERR_INVALID;
@@ -186,6 +192,11 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
     a.grid_x = p.grid_x;
     a.q_bf16 = c.q_type == MLA_FA_BF16;
     a.scale_log2 = c.scale * 1.4426950408889634f;
+    a.kv_len = c.kv_len;
+    a.alibi = c.alibi;
+    a.sinks = c.sinks;
+    a.cap_in = c.softcap > 0.f ? c.scale / c.softcap : 0.f;
+    a.cap_out = c.softcap * 1.4426950408889634f;
     if (std::getenv("MLA_FA_LOG"))
         fprintf(stderr, "mla_fa: rows=%lld heads=%d n_kv=%lld split=%d chunk=%lld shape=%d hg=%d grid=%dx%lld\n",
                 (long long)n_rows, c.n_head, (long long)c.n_kv, p.n_split, (long long)p.split_chunk,
@@ -195,11 +206,12 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
 }
 
 int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *ws, size_t ws_bytes,
-              hipStream_t stream) {
+              hipStream_t stream, const float *sinks = nullptr) {
     if (n_split <= 1) return MLA_FA_OK;
     const size_t need = partial_bytes(n_rows, n_head, n_split);
     if (!ws || ws_bytes < need || !aligned(ws, 16)) return MLA_FA_ERR_WORKSPACE;
-    hipError_t e = launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws), out, stream);
+    hipError_t e = launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws), out, sinks,
+                                stream);
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -310,6 +322,32 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
     st = run_partials(c, p, s);
     if (st) return st;
     return run_merge(n_tok, n_head, p.n_split, out, workspace, workspace_bytes, s);
+}
+
+int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                  int64_t kv_seq_stride, int n_seq, int n_tok, int n_head, int64_t n_kv,
+                  const int32_t *kv_len, int causal, const uint16_t *mask, int64_t mask_seq_stride,
+                  int64_t mask_tok_stride, const float *alibi_slopes, const float *sinks, float softcap,
+                  float scale, float *out, int n_split, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    Common c;
+    c.q = q; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
+    c.kv_row_stride = kv_row_stride; c.kv_seq_stride = kv_seq_stride;
+    c.n_seq = n_seq; c.n_tok = n_tok; c.n_head = n_head; c.n_kv = n_kv; c.causal = causal;
+    c.mask = mask; c.mask_seq_stride = mask_seq_stride; c.mask_tok_stride = mask_tok_stride;
+    c.kv_idx = nullptr; c.kv_idx_count = nullptr; c.idx_seq_stride = 0;
+    c.scale = scale; c.out = out; c.n_split = n_split; c.ws = workspace; c.ws_bytes = workspace_bytes;
+    c.kv_len = kv_len; c.alibi = alibi_slopes; c.sinks = sinks; c.softcap = softcap;
+    int st = validate(c);
+    if (st) return st;
+    const int64_t n_rows = (int64_t)n_seq * n_tok;
+    Plan p = make_plan(n_rows, n_head, n_kv, kv_type, n_split);
+    if (p.n_split > 1 && (!workspace || workspace_bytes < partial_bytes(n_rows, n_head, p.n_split)))
+        return MLA_FA_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_partials(c, p, s);
+    if (st) return st;
+    return run_merge(n_rows, n_head, p.n_split, out, workspace, workspace_bytes, s, sinks);
 }
 
 int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,

@@ -204,6 +204,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         chunk = (kend + a.n_split - 1) / a.n_split;
         chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
         if (chunk == 0) chunk = kTileKeys;
+    } else if (a.kv_len) {
+        // per-sequence valid length; the split chunk follows the row's own range
+        int64_t len = a.kv_len[s_idx];
+        len = len < 0 ? 0 : (len > a.n_kv ? a.n_kv : len);
+        kend = a.causal ? len - a.n_tok + t_idx + 1 : len;
+        if (kend < 0) kend = 0;
+        chunk = (kend + a.n_split - 1) / a.n_split;
+        chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+        if (chunk == 0) chunk = kTileKeys;
     } else {
         kend = a.causal ? a.n_kv - a.n_tok + t_idx + 1 : a.n_kv;
     }
@@ -273,6 +282,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         l_run[mb] = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 32; ++nb) o[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // ALiBi slope of this lane's head (scaled to log2 units), per 16-head block
+    float slope_l2[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int head = h_base + mb * 16 + l16;
+        slope_l2[mb] = a.alibi && head < a.n_head ? a.alibi[head] * kLog2e : kLog2e;
     }
 
     // ---- per-lane LDS read offsets (relative to a sub-tile), tile-invariant
@@ -457,15 +473,32 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             float tv[8];
+            if (a.cap_in != 0.f) {
+                // logit softcap: cap * tanh(scale * dot / cap), tanh(y) = 1 - 2 / (e^(2y) + 1)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) tv[i] = sacc[i >> 2][mb][i & 3] * a.scale_log2;
+                for (int i = 0; i < 8; ++i) {
+                    const float e2y = __builtin_amdgcn_exp2f(sacc[i >> 2][mb][i & 3] * a.cap_in * (2.f * kLog2e));
+                    tv[i] = a.cap_out * (1.f - 2.f * __builtin_amdgcn_rcpf(e2y + 1.f));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) tv[i] = sacc[i >> 2][mb][i & 3] * a.scale_log2;
+            }
             if (mrow) {
                 const unsigned *mls = reinterpret_cast<const unsigned *>(mask_lds);
                 const u32x4 mk[2] = {*reinterpret_cast<const u32x4 *>(mls + sub0 + 4 * g),
                                      *reinterpret_cast<const u32x4 *>(mls + sub0 + 16 + 4 * g)};
+                if (a.alibi) {   // slope * mask value for kept cells; -inf stays -inf
 #pragma unroll
-                for (int i = 0; i < 8; ++i)   // key k's mask: low half of dword k
-                    tv[i] += f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e;
+                    for (int i = 0; i < 8; ++i) {
+                        const unsigned short mbits = (unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu);
+                        tv[i] += mbits == 0xFC00u ? -INFINITY : f16_bits_to_f32(mbits) * slope_l2[mb];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)   // key k's mask: low half of dword k
+                        tv[i] += f16_bits_to_f32((unsigned short)(mk[i >> 2][i & 3] & 0xFFFFu)) * kLog2e;
+                }
             }
             if (rem64 < kSub) {
                 const int rem = (int)rem64;
@@ -626,7 +659,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     if (a.n_split == 1) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const float inv = l_run[mb] > 0.f ? 1.f / l_run[mb] : 0.f;
+            float lt = l_run[mb];
+            if (a.sinks && m_run[mb] != -INFINITY) {   // the sink joins the normaliser
+                const int head = h_base + mb * 16 + l16;
+                if (head < a.n_head) lt += __builtin_amdgcn_exp2f(a.sinks[head] * kLog2e - m_run[mb]);
+            }
+            const float inv = l_run[mb] > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float ir = shfl_f(inv, 4 * g + r);
@@ -1115,7 +1153,8 @@ constexpr int kMergeGroups = kMergeThreads / 128;
 constexpr int kMergeBatch = 8;
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_head, int n_split,
                                                               const float *__restrict__ ws,
-                                                              float *__restrict__ out) {
+                                                              float *__restrict__ out,
+                                                              const float *__restrict__ sinks) {
     __shared__ float w_s[kMaxSplits];
     __shared__ float l_s[kMaxSplits];
     __shared__ float red[kMergeThreads / 64];
@@ -1164,6 +1203,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < kMergeThreads / 64; ++i) lsum += red[i];
+    if (sinks && mstar != -INFINITY)   // the sink joins the normaliser (m* in log2 units)
+        lsum += __builtin_amdgcn_exp2f(sinks[rh % n_head] * 1.4426950408889634f - mstar);
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1205,6 +1246,9 @@ hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Per-sequence lengths, ALiBi, sinks and softcap run in the single-wave kernel only.
+bool uses_extras(const AttnArgs &a) { return a.kv_len || a.alibi || a.sinks || a.cap_in != 0.f; }
+
 template <int NP, int KIND, bool IDX>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t stream) {
     dim3 grid(a.grid_x, a.n_seq * a.n_tok);
@@ -1222,10 +1266,12 @@ hipError_t launch_shape(const AttnArgs &a, int shape, hipStream_t stream) {
         // pair shapes: dense 16-bit caches only; Q8_0 and indexed rows run the single-wave
         // kernel with the same heads per workgroup (so the plan's head groups still hold)
         case SHAPE_P64:
-            if constexpr (KIND != KV_Q8 && !IDX) return launch_pair<2, KIND, IDX>(a, stream);
+            if constexpr (KIND != KV_Q8 && !IDX)
+                if (!uses_extras(a)) return launch_pair<2, KIND, IDX>(a, stream);
             return launch_one<1, 8, 2, KIND, IDX>(a, stream);
         case SHAPE_P128:
-            if constexpr (KIND != KV_Q8 && !IDX) return launch_pair<4, KIND, IDX>(a, stream);
+            if constexpr (KIND != KV_Q8 && !IDX)
+                if (!uses_extras(a)) return launch_pair<4, KIND, IDX>(a, stream);
             return launch_one<1, 8, 1, KIND, IDX>(a, stream);
     }
     return hipErrorInvalidValue;
@@ -1248,9 +1294,9 @@ hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream
 }
 
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
-                        hipStream_t stream) {
+                        const float *sinks, hipStream_t stream) {
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)n_rows * n_head)), dim3(kMergeThreads), 0,
-                       stream, n_rows, n_head, n_split, ws, out);
+                       stream, n_rows, n_head, n_split, ws, out, sinks);
     return hipGetLastError();
 }
 

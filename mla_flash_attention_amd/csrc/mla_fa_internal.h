@@ -42,6 +42,11 @@ struct AttnArgs {
     int grid_x;                    // blockIdx.x extent (head_groups * splits, padded)
     int q_bf16;                    // q bits are bf16 (else f16)
     float scale_log2;              // scale * log2(e)
+    const int32_t *kv_len;         // [n_seq] valid cells per sequence, or nullptr (= n_kv)
+    const float *alibi;            // [n_head] slope multiplying the mask of kept cells, or nullptr
+    const float *sinks;            // [n_head] sink logits (natural log), or nullptr
+    float cap_in;                  // softcap: score = cap_out * tanh(dot * cap_in) in log2 units;
+    float cap_out;                 //   cap_in = 0 means no softcap
 };
 
 // Partial layout inside the workspace, for R = n_seq*n_tok rows, H heads, S splits:
@@ -52,7 +57,7 @@ inline size_t partial_bytes(int64_t rows, int heads, int splits) {
 
 hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
-                        hipStream_t stream);
+                        const float *sinks, hipStream_t stream);
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,
                           hipStream_t stream);

@@ -120,3 +120,30 @@ def test_merge_validation(L):
     assert L.mla_fa_merge_partials(0, 128, 8, FAKE, FAKE, 1 << 30, None) == B.MLA_FA_ERR_INVALID
     # n_split == 1 has nothing to merge
     assert L.mla_fa_merge_partials(4, 128, 1, FAKE, None, 0, None) == B.MLA_FA_OK
+
+
+def _attend(L, **kw):
+    a = dict(q=FAKE, qt=B.MLA_FA_BF16, kv=FAKE, kvt=B.MLA_FA_BF16, rs=1152, ss=1152 * 64, n_seq=2, n_tok=2,
+             H=128, n_kv=64, kv_len=None, causal=0, mask=None, ms=0, mt=0, alibi=None, sinks=None,
+             softcap=0.0, scale=0.1, out=FAKE, n_split=1, ws=None, wsb=0)
+    a.update(kw)
+    return L.mla_fa_attend(a["q"], a["qt"], a["kv"], a["kvt"], a["rs"], a["ss"], a["n_seq"], a["n_tok"],
+                           a["H"], a["n_kv"], a["kv_len"], a["causal"], a["mask"], a["ms"], a["mt"],
+                           a["alibi"], a["sinks"], ctypes.c_float(a["softcap"]), ctypes.c_float(a["scale"]),
+                           a["out"], a["n_split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(softcap=-1.0), B.MLA_FA_ERR_INVALID),                      # negative softcap
+    (dict(softcap=float("inf")), B.MLA_FA_ERR_INVALID),              # non-finite softcap
+    (dict(kv_len=FAKE + 2), B.MLA_FA_ERR_INVALID),                   # misaligned lengths
+    (dict(alibi=FAKE + 1), B.MLA_FA_ERR_INVALID),                    # misaligned slopes
+    (dict(sinks=FAKE + 2), B.MLA_FA_ERR_INVALID),                    # misaligned sinks
+    (dict(causal=1, n_tok=65), B.MLA_FA_ERR_INVALID),                # causal, no lengths, n_tok > n_kv
+    (dict(n_tok=0), B.MLA_FA_ERR_INVALID),                           # no query token
+    (dict(H=120), B.MLA_FA_ERR_UNSUPPORTED),                         # heads not a multiple of 16
+    (dict(qt=B.MLA_FA_F16, kvt=B.MLA_FA_BF16), B.MLA_FA_ERR_UNSUPPORTED),
+    (dict(n_split=4, ws=FAKE, wsb=16), B.MLA_FA_ERR_WORKSPACE),      # workspace too small
+])
+def test_attend_validation(L, kw, status):
+    assert _attend(L, **kw) == status
