@@ -186,6 +186,35 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0):
                 merge_ms=merge_ms, compact_ms=compact_ms, n_split=ns, kept=kept)
 
 
+def _time_attend(B, p, steps, warmup, n_split=0):
+    """Back-to-back mla_fa_attend calls (attention + merge) between two events."""
+    import torch
+    stream = torch.cuda.current_stream()
+    q = _dev(p.q)
+    kv = _dev(p.kv)
+    out = torch.empty((p.n_seq, p.n_tok, p.n_head, 512), dtype=torch.float32, device="cuda")
+    mask = None if p.mask is None else _dev(p.mask)
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kv_len, alibi, sinks = f(p.kv_len), f(p.alibi), f(p.sinks)
+    ns = n_split or B.mla_fa_auto_splits(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type)
+    ws = B.workspace_for(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type, ns)
+
+    def call():
+        B.mla_fa_attend(q, p.q_type, kv, p.kv_type, p.scale, out, kv_len=kv_len, causal=p.causal, mask=mask,
+                        alibi=alibi, sinks=sinks, softcap=p.softcap, n_split=ns, workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return dict(step_ms=t0.elapsed_time(t1) / steps, n_split=ns)
+
+
 def _time_prefill(B, p, steps, warmup):
     import torch
     from mla_flash_attention_amd import synth
@@ -310,6 +339,22 @@ def main():
                                                  kept=r["kept"], n_split=r["n_split"],
                                                  scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
                                                  kept_cells_per_s=r["kept"] / (r["step_ms"] * 1e-3))
+        if want("n3"):
+            # ragged multi-token decode: 8 sequences of U{2..32768} valid cells, 2 query tokens
+            # each (causal), 128 heads; plain, then with softcap 50, sinks and ALiBi over a
+            # distance mask
+            for tag, kw in (("plain", {}), ("softcap_sinks_alibi", dict(softcap=50.0, sinks=True, alibi=True,
+                                                                         mask_kind="distance"))):
+                p = synth.make_problem(kind="decode", n_seq=8, n_tok=2, n_head=128, n_kv=32768, seed=6,
+                                       ragged=True, causal=True, **kw)
+                r = _time_attend(B, p, args.steps, args.warmup)
+                lens = p.kv_len.astype(np.int64)
+                cells = int(sum(L - p.n_tok + t + 1 for L in lens for t in range(p.n_tok)))
+                cache_bytes = int(lens.sum()) * 1152
+                sec[f"n3_ragged_2tok_decode_{tag}"] = dict(
+                    ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3), n_split=r["n_split"],
+                    cache_bytes_once=cache_bytes,
+                    hbm_frac_cache_once=cache_bytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
     if sec:
         result["secondary"] = sec
     if args.copy_calibration:
