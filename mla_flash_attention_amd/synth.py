@@ -249,3 +249,38 @@ def make_config(cfg_id: int, seed: int | None = None, **overrides) -> Problem:
     spec = dict(CONFIGS[cfg_id])
     spec.update(overrides)
     return make_problem(seed=cfg_id if seed is None else seed, **spec)
+
+
+# ---------------------------------------------------------------- per-head (non-absorbed) shape
+MHA_DK = 192       # 128 per-head dims + 64 RoPE
+MHA_DV = 128
+
+
+@dataclasses.dataclass
+class MhaProblem:
+    """Per-head attention with separate K and V (bits): q [n_tok][n_head][192],
+    k [n_kv][n_head][192], v [n_kv][n_head][128]; mask [n_tok][n_kv] f16 bits or None."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_type: int
+    kv_type: int
+    n_tok: int
+    n_head: int
+    n_kv: int
+    scale: np.float32
+    causal: bool = True
+    mask: np.ndarray | None = None
+
+
+def make_mha_problem(n_tok: int, n_head: int, n_kv: int, q_type: int = TYPE_BF16, kv_type: int = TYPE_BF16,
+                     seed: int = 0, causal: bool = True, mask_kind: str | None = None,
+                     scale: float | None = None) -> MhaProblem:
+    """Streams: 0 = Q, 1 = K, 5 = V, 2 = mask; N(0,1) values rounded to the storage type;
+    scale defaults to 1/sqrt(192) in fp32."""
+    q = round_bits(rng(seed, 0).standard_normal((n_tok, n_head, MHA_DK), dtype=np.float32), q_type)
+    k = round_bits(rng(seed, 1).standard_normal((n_kv, n_head, MHA_DK), dtype=np.float32), kv_type)
+    v = round_bits(rng(seed, 5).standard_normal((n_kv, n_head, MHA_DV), dtype=np.float32), kv_type)
+    mask = None if mask_kind is None else make_mask(mask_kind, 1, n_tok, n_kv, rng(seed, 2))[0]
+    return MhaProblem(q=q, k=k, v=v, q_type=q_type, kv_type=kv_type, n_tok=n_tok, n_head=n_head, n_kv=n_kv,
+                      scale=np.float32(DEFAULT_SCALE if scale is None else scale), causal=causal, mask=mask)

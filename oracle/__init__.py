@@ -48,6 +48,12 @@ def _lib():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
             ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        lib.oracle_mha_attention.restype = ctypes.c_int64
+        lib.oracle_mha_attention.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_mask_compact.restype = None
         lib.oracle_mask_compact.argtypes = [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
@@ -139,6 +145,32 @@ def attention_problem(p, rows=None, return_stats=False):
                      return_stats=return_stats, kv_len=getattr(p, "kv_len", None),
                      alibi=getattr(p, "alibi", None), sinks=getattr(p, "sinks", None),
                      softcap=getattr(p, "softcap", 0.0))
+
+
+def mha_attention(q, q_type, k, v, kv_type, scale, *, causal=False, mask=None, rows=None):
+    """fp64 per-head attention with separate K and V: q uint16 [n_tok][n_head][dk],
+    k uint16 [n_kv][n_head][dk], v uint16 [n_kv][n_head][dv], mask uint16 [n_tok][n_kv] or
+    None -> [len(rows) or n_tok*n_head][dv] (rows: flat ids t*n_head + h)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    n_tok, n_head, dk = q.shape
+    n_kv, dv = k.shape[0], v.shape[-1]
+    assert k.shape == (n_kv, n_head, dk) and v.shape == (n_kv, n_head, dv)
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.uint16).reshape(n_tok, n_kv)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.size
+    else:
+        n_rows = n_tok * n_head
+    out = np.zeros((n_rows, dv), dtype=np.float64)
+    rc = _lib().oracle_mha_attention(
+        _ptr(q), q_type, _ptr(k), _ptr(v), kv_type, n_head * dk, n_head * dv, n_tok, n_head, n_kv, dk, dv,
+        1 if causal else 0, _ptr(mask), n_kv, float(np.float32(scale)), _ptr(rows), n_rows, _ptr(out))
+    if rc < 0:
+        raise ValueError(f"oracle_mha_attention failed ({rc})")
+    return out
 
 
 def mask_compact(mask2d: np.ndarray):

@@ -264,6 +264,77 @@ int64_t oracle_mla_attention(const uint16_t *q, int q_type, const uint8_t *kv, i
                                     row_max, row_sum);
 }
 
+/*
+ * Per-head attention with separate K and V (the non-absorbed MLA prefill shape, e.g.
+ * dk = 192 = 128 + 64 RoPE, dv = 128), out[i][d] for each selected row i = t*n_head + h:
+ *
+ *   q    : bits [n_tok][n_head][dk], f16 or bf16
+ *   k    : bits, key j of head h at k + j*k_row_stride + h*dk (elements), f16 or bf16
+ *   v    : bits, value j of head h at v + j*v_row_stride + h*dv (elements), same type as k
+ *   causal : token t sees keys j <= n_kv - n_tok + t
+ *   mask : f16 bits [n_tok][mask_row_stride] or NULL (-inf drops a key, else added)
+ * score_j = scale * q.k_j + mask_j, softmax over kept keys, out = sum_j p_j v_j
+ * (zeros for a row with no kept key).  Returns the number of such rows, or < 0 on bad input.
+ */
+int64_t oracle_mha_attention(const uint16_t *q, int q_type, const uint16_t *k, const uint16_t *v,
+                             int kv_type, int64_t k_row_stride, int64_t v_row_stride, int n_tok,
+                             int n_head, int64_t n_kv, int dk, int dv, int causal,
+                             const uint16_t *mask, int64_t mask_row_stride, double scale,
+                             const int64_t *rows, int64_t n_rows, double *out) {
+    if (!q || !k || !v || !out || n_tok < 1 || n_head < 1 || n_kv < 1 || dk < 1 || dv < 1) return -1;
+    if ((q_type != OR_F16 && q_type != OR_BF16) || (kv_type != OR_F16 && kv_type != OR_BF16)) return -1;
+    const int64_t total = (int64_t)n_tok * n_head;
+    if (!rows) n_rows = total;
+    int64_t n_empty = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : n_empty)
+    for (int64_t i = 0; i < n_rows; ++i) {
+        const int64_t r = rows ? rows[i] : i;
+        double *o = out + i * dv;
+        for (int d = 0; d < dv; ++d) o[d] = 0.0;
+        if (r < 0 || r >= total) continue;
+        const int t = (int)(r / n_head), h = (int)(r % n_head);
+        double *qv = (double *)malloc((size_t)dk * sizeof(double));
+        double *kv_ = (double *)malloc((size_t)dk * sizeof(double));
+        double *vv = (double *)malloc((size_t)dv * sizeof(double));
+        double *score = (double *)malloc((size_t)n_kv * sizeof(double));
+        decode_row((const uint8_t *)(q + r * dk), q_type, dk, qv);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n_kv; ++j) {
+            double bias = mask ? oracle_f16_to_f64(mask[(int64_t)t * mask_row_stride + j]) : 0.0;
+            if (causal && j > n_kv - n_tok + t) bias = -INFINITY;
+            if (bias == -INFINITY) {
+                score[j] = -INFINITY;
+                continue;
+            }
+            decode_row((const uint8_t *)(k + j * k_row_stride + (int64_t)h * dk), kv_type, dk, kv_);
+            double dot = 0.0;
+            for (int d = 0; d < dk; ++d) dot += qv[d] * kv_[d];
+            score[j] = scale * dot + bias;
+            if (score[j] > m) m = score[j];
+        }
+        if (m == -INFINITY) {
+            n_empty += 1;
+        } else {
+            double l = 0.0;
+            for (int64_t j = 0; j < n_kv; ++j) {
+                score[j] = score[j] == -INFINITY ? 0.0 : exp(score[j] - m);
+                l += score[j];
+            }
+            for (int64_t j = 0; j < n_kv; ++j) {
+                if (score[j] == 0.0) continue;
+                decode_row((const uint8_t *)(v + j * v_row_stride + (int64_t)h * dv), kv_type, dv, vv);
+                const double p = score[j] / l;
+                for (int d = 0; d < dv; ++d) o[d] += p * vv[d];
+            }
+        }
+        free(qv);
+        free(kv_);
+        free(vv);
+        free(score);
+    }
+    return n_empty;
+}
+
 /* Sparse-mask index compaction: for each mask row, the ascending list of cells
  * whose f16 mask is not -inf (bits != 0xFC00), and its length. */
 void oracle_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
