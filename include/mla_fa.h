@@ -177,6 +177,35 @@ int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_
                   void *stream);
 
 /*
+ * Per-head attention with separate keys and values: the non-absorbed MLA shape, where
+ * every head has its own 192-wide key (128 dims + 64 RoPE) and 128-wide value
+ * ("llama.cpp Metal: tensor-API flash attention for F16 KV caches" news item lists
+ * DK=192 / DV=128 beside 576/512; "Vulkan backend fused Flash Attention: DeepSeek MLA
+ * local inference", section 3.3, describes the decompressed per-head K and V).  Same
+ * online softmax and mask convention as the latent entry points; for token t, head h:
+ *     s_j = scale * <q[t][h], k[j][h]> + mask[t][j]     (-inf past the causal edge)
+ *     out[t][h] = sum_j softmax(s)_j * v[j][h]           (zeros when no key is kept)
+ *   q        [n_tok][n_head][192] f16/bf16 bits (device), 16-byte aligned.
+ *   k, v     key j of head h at k + j*k_row_stride + h*384 and v + j*v_row_stride + h*256
+ *            (bytes; device; 16-byte aligned, strides multiples of 16 and at least
+ *            n_head*384 and n_head*256).  kv_type must equal q_type (f16 or bf16).
+ *   causal   nonzero: token t attends to keys j <= n_kv - n_tok + t; requires n_tok <= n_kv.
+ *   mask     NULL, or f16 bits, token t's row at mask + t*mask_row_stride (elements),
+ *            8-byte aligned with mask_row_stride a multiple of 4 (>= n_kv when n_tok > 1).
+ *            It is read in aligned 8-byte words: the word holding key n_kv - 1 may reach
+ *            up to 3 elements past the row; those values are never used.
+ *   out      [n_tok][n_head][128] fp32 (device), 16-byte aligned.
+ * One launch, no workspace: a workgroup holds 256 tokens of one head in registers and
+ * streams that head's keys and values through LDS.  1 <= n_head <= 65535,
+ * 1 <= n_kv <= 2^31-1.  Errors: ERR_INVALID for null pointers, sizes, strides and
+ * alignment as above; ERR_UNSUPPORTED for other type pairs.
+ */
+int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, int kv_type,
+                       int64_t k_row_stride, int64_t v_row_stride, int n_tok, int n_head, int64_t n_kv,
+                       int causal, const uint16_t *mask, int64_t mask_row_stride, float scale,
+                       float *out, void *stream);
+
+/*
  * Sparse-mask index compaction.  For each of n_rows f16 mask rows (row r at
  * mask + r*mask_row_stride elements, n_kv cells), writes the ascending list of cells
  * whose mask is not -inf (bit pattern != 0xFC00) to idx + r*idx_row_stride and its

@@ -22,7 +22,7 @@ MLA_FA_OK, MLA_FA_ERR_INVALID, MLA_FA_ERR_UNSUPPORTED, MLA_FA_ERR_WORKSPACE, MLA
 
 EXPORTS = ("mla_fa_strerror", "mla_fa_version", "mla_fa_auto_splits", "mla_fa_workspace_size",
            "mla_fa_decode", "mla_fa_decode_partials", "mla_fa_merge_partials", "mla_fa_prefill",
-           "mla_fa_attend", "fa_mask_compact")
+           "mla_fa_attend", "mla_fa_prefill_mha", "fa_mask_compact")
 
 _LIB = None
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.mla_fa_attend.restype = _i
         L.mla_fa_attend.argtypes = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64, _i64,
                                     _p, _p, _f, _f, _p, _i, _p, _sz, _p]
+        L.mla_fa_prefill_mha.restype = _i
+        L.mla_fa_prefill_mha.argtypes = [_p, _i, _p, _p, _i, _i64, _i64, _i, _i, _i64, _i, _p, _i64, _f, _p, _p]
         _LIB = L
     return _LIB
 
@@ -180,6 +182,20 @@ def mla_fa_attend(q, q_type, kv, kv_type, scale, out, *, kv_len=None, causal=Fal
                                float(softcap), float(scale), _ptr(out), n_split, _ptr(workspace), ws_bytes,
                                _stream(stream)),
            "mla_fa_attend")
+    return out
+
+
+def mla_fa_prefill_mha(q, q_type, k, v, kv_type, scale, out, *, causal=True, mask=None, stream=None):
+    """q [n_tok][n_head][192], k [n_kv][n_head][192], v [n_kv][n_head][128] (16-bit bits;
+    k and v rows may be strided), out fp32 [n_tok][n_head][128]; mask [n_tok][>=n_kv] f16
+    bits with a row stride that is a multiple of 4."""
+    n_tok, n_head = q.shape[0], q.shape[1]
+    n_kv = k.shape[0]
+    _check(lib().mla_fa_prefill_mha(_ptr(q), q_type, _ptr(k), _ptr(v), kv_type, k.stride(0) * k.element_size(),
+                                    v.stride(0) * v.element_size(), n_tok, n_head, n_kv, 1 if causal else 0,
+                                    _ptr(mask), 0 if mask is None else mask.stride(0), float(scale), _ptr(out),
+                                    _stream(stream)),
+           "mla_fa_prefill_mha")
     return out
 
 

@@ -350,6 +350,44 @@ int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_
     return run_merge(n_rows, n_head, p.n_split, out, workspace, workspace_bytes, s, sinks);
 }
 
+int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, int kv_type,
+                       int64_t k_row_stride, int64_t v_row_stride, int n_tok, int n_head, int64_t n_kv,
+                       int causal, const uint16_t *mask, int64_t mask_row_stride, float scale,
+                       float *out, void *stream) {
+    if (!q || !k || !v || !out) return MLA_FA_ERR_INVALID;
+    if (q_type != MLA_FA_F16 && q_type != MLA_FA_BF16) return MLA_FA_ERR_INVALID;
+    if (kv_type != MLA_FA_F16 && kv_type != MLA_FA_BF16 && kv_type != MLA_FA_Q8_0) return MLA_FA_ERR_INVALID;
+    if (kv_type != q_type) return MLA_FA_ERR_UNSUPPORTED;
+    if (n_tok < 1 || n_head < 1 || n_head > 65535 || n_kv < 1 || n_kv > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
+    if (causal && n_tok > n_kv) return MLA_FA_ERR_INVALID;
+    if (!std::isfinite(scale)) return MLA_FA_ERR_INVALID;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return MLA_FA_ERR_INVALID;
+    if (k_row_stride < (int64_t)n_head * 384 || k_row_stride % 16 || v_row_stride < (int64_t)n_head * 256 ||
+        v_row_stride % 16)
+        return MLA_FA_ERR_INVALID;
+    if (mask) {
+        if (!aligned(mask, 8) || mask_row_stride < 0 || mask_row_stride % 4) return MLA_FA_ERR_INVALID;
+        if (n_tok > 1 && mask_row_stride < n_kv) return MLA_FA_ERR_INVALID;
+    }
+    MhaArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint8_t *>(k);
+    a.v = static_cast<const uint8_t *>(v);
+    a.k_row_stride = k_row_stride;
+    a.v_row_stride = v_row_stride;
+    a.mask = mask;
+    a.mask_row_stride = mask_row_stride;
+    a.out = out;
+    a.n_kv = n_kv;
+    a.n_tok = n_tok;
+    a.n_head = n_head;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e = launch_mha(a, kv_kind_of(kv_type), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
 int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                     int32_t *idx, int64_t idx_row_stride, int32_t *count, void *stream) {
     if (!mask || !idx || !count || n_rows < 1 || n_kv < 1 || n_kv > 0x7FFFFFFFLL)

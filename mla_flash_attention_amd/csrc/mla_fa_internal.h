@@ -55,9 +55,26 @@ inline size_t partial_bytes(int64_t rows, int heads, int splits) {
     return (size_t)splits * rows * heads * (2 + kDV) * sizeof(float);
 }
 
+// Per-head attention with separate K (192 wide) and V (128 wide), 16-bit types.
+struct MhaArgs {
+    const uint16_t *q;             // [n_tok][n_head][192]
+    const uint8_t *k;              // key j, head h at k + j * k_row_stride + h * 384
+    const uint8_t *v;              // key j, head h at v + j * v_row_stride + h * 256
+    int64_t k_row_stride;          // bytes
+    int64_t v_row_stride;          // bytes
+    const uint16_t *mask;          // f16 bits, token t at mask + t * mask_row_stride, or nullptr
+    int64_t mask_row_stride;       // elements, a multiple of 4 (8-byte mask loads)
+    float *out;                    // [n_tok][n_head][128] fp32
+    int64_t n_kv;
+    int n_tok, n_head;
+    int causal;                    // token t sees keys j <= n_kv - n_tok + t
+    float scale_log2;              // scale * log2(e)
+};
+
 hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
                         const float *sinks, hipStream_t stream);
+hipError_t launch_mha(const MhaArgs &a, int kv_kind, hipStream_t stream);
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,
                           hipStream_t stream);

@@ -147,3 +147,34 @@ def _attend(L, **kw):
 ])
 def test_attend_validation(L, kw, status):
     assert _attend(L, **kw) == status
+
+
+def _mha(L, **kw):
+    a = dict(q=FAKE, qt=B.MLA_FA_BF16, k=FAKE, v=FAKE, kvt=B.MLA_FA_BF16, ks=128 * 384, vs=128 * 256, n_tok=8,
+             H=128, n_kv=16, causal=1, mask=None, ms=0, scale=0.1, out=FAKE)
+    a.update(kw)
+    return L.mla_fa_prefill_mha(a["q"], a["qt"], a["k"], a["v"], a["kvt"], a["ks"], a["vs"], a["n_tok"], a["H"],
+                                a["n_kv"], a["causal"], a["mask"], a["ms"], ctypes.c_float(a["scale"]), a["out"],
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.MLA_FA_ERR_INVALID),
+    (dict(v=None), B.MLA_FA_ERR_INVALID),
+    (dict(n_tok=17), B.MLA_FA_ERR_INVALID),                          # causal chunk longer than the cache
+    (dict(n_tok=0), B.MLA_FA_ERR_INVALID),
+    (dict(n_kv=0), B.MLA_FA_ERR_INVALID),
+    (dict(H=0), B.MLA_FA_ERR_INVALID),
+    (dict(ks=128 * 384 - 16), B.MLA_FA_ERR_INVALID),                 # key rows overlap
+    (dict(vs=128 * 256 + 8), B.MLA_FA_ERR_INVALID),                  # value stride not a multiple of 16
+    (dict(k=FAKE + 8), B.MLA_FA_ERR_INVALID),                        # misaligned keys
+    (dict(mask=FAKE + 2, ms=16), B.MLA_FA_ERR_INVALID),              # mask not 8-byte aligned
+    (dict(mask=FAKE, ms=18), B.MLA_FA_ERR_INVALID),                  # mask stride not a multiple of 4
+    (dict(mask=FAKE, ms=12), B.MLA_FA_ERR_INVALID),                  # mask rows shorter than n_kv
+    (dict(scale=float("nan")), B.MLA_FA_ERR_INVALID),
+    (dict(qt=B.MLA_FA_F16), B.MLA_FA_ERR_UNSUPPORTED),               # q and cache types differ
+    (dict(qt=B.MLA_FA_Q8_0, kvt=B.MLA_FA_Q8_0), B.MLA_FA_ERR_INVALID),
+    (dict(kvt=B.MLA_FA_Q8_0), B.MLA_FA_ERR_UNSUPPORTED),
+])
+def test_prefill_mha_validation(L, kw, status):
+    assert _mha(L, **kw) == status
