@@ -235,6 +235,35 @@ def _time_prefill(B, p, steps, warmup):
     return dict(step_ms=float(np.mean(ms)), p10=float(np.percentile(ms, 10)), p90=float(np.percentile(ms, 90)))
 
 
+def _time_mha(B, p, steps, warmup):
+    """Back-to-back mla_fa_prefill_mha calls between two events, and single-launch p10/p90."""
+    import torch
+    stream = torch.cuda.current_stream()
+    q, k, v = _dev(p.q), _dev(p.k), _dev(p.v)
+    out = torch.empty((p.n_tok, p.n_head, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        B.mla_fa_prefill_mha(q, p.q_type, k, v, p.kv_type, p.scale, out, causal=p.causal, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        call()
+        evs[i][1].record(stream)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return dict(step_ms=t0.elapsed_time(t1) / steps, p10=float(np.percentile(ms, 10)),
+                p90=float(np.percentile(ms, 90)))
+
+
 def _algo_decode(p, kept=None):
     """Algorithmic bytes and flops of one decode call: cache rows attended, Q, O (and the
     mask/index traffic of the sparse path); flops 2*H*(576+512) per attended cell."""
@@ -321,6 +350,16 @@ def main():
             sec["c3_prefill_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
                                                       cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
                                                       mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
+        if want("n2"):
+            # non-absorbed MLA prefill: per-head 192-wide keys, 128-wide values, the C3 chunk shape
+            p = synth.make_mha_problem(2048, 128, 4096, synth.TYPE_BF16, synth.TYPE_BF16, seed=3, causal=True)
+            r = _time_mha(B, p, max(5, args.steps // 5), max(2, args.warmup // 5))
+            pairs = sum(p.n_kv - p.n_tok + t + 1 for t in range(p.n_tok))
+            fl = pairs * 2 * p.n_head * (192 + 128)
+            tf = fl / (r["step_ms"] * 1e-3) / 1e12
+            sec["n2_prefill_mha_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
+                                                          cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
+                                                          mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
         if want("c4"):
             p = synth.make_config(4)
             r = _time_decode(B, p, args.copies, args.steps, args.warmup)

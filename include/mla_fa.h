@@ -191,9 +191,9 @@ int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_
  *            n_head*384 and n_head*256).  kv_type must equal q_type (f16 or bf16).
  *   causal   nonzero: token t attends to keys j <= n_kv - n_tok + t; requires n_tok <= n_kv.
  *   mask     NULL, or f16 bits, token t's row at mask + t*mask_row_stride (elements),
- *            8-byte aligned with mask_row_stride a multiple of 4 (>= n_kv when n_tok > 1).
- *            It is read in aligned 8-byte words: the word holding key n_kv - 1 may reach
- *            up to 3 elements past the row; those values are never used.
+ *            16-byte aligned with mask_row_stride a multiple of 8 (>= n_kv when n_tok > 1).
+ *            It is read in aligned 16-byte blocks: the block holding key n_kv - 1 may reach
+ *            up to 7 elements past the row; those values are never used.
  *   out      [n_tok][n_head][128] fp32 (device), 16-byte aligned.
  * One launch, no workspace: a workgroup holds 256 tokens of one head in registers and
  * streams that head's keys and values through LDS.  1 <= n_head <= 65535,

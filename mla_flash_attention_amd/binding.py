@@ -188,7 +188,7 @@ def mla_fa_attend(q, q_type, kv, kv_type, scale, out, *, kv_len=None, causal=Fal
 def mla_fa_prefill_mha(q, q_type, k, v, kv_type, scale, out, *, causal=True, mask=None, stream=None):
     """q [n_tok][n_head][192], k [n_kv][n_head][192], v [n_kv][n_head][128] (16-bit bits;
     k and v rows may be strided), out fp32 [n_tok][n_head][128]; mask [n_tok][>=n_kv] f16
-    bits with a row stride that is a multiple of 4."""
+    bits, 16-byte aligned, with a row stride that is a multiple of 8."""
     n_tok, n_head = q.shape[0], q.shape[1]
     n_kv = k.shape[0]
     _check(lib().mla_fa_prefill_mha(_ptr(q), q_type, _ptr(k), _ptr(v), kv_type, k.stride(0) * k.element_size(),

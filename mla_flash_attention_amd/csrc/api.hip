@@ -360,13 +360,14 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
     if (kv_type != q_type) return MLA_FA_ERR_UNSUPPORTED;
     if (n_tok < 1 || n_head < 1 || n_head > 65535 || n_kv < 1 || n_kv > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
     if (causal && n_tok > n_kv) return MLA_FA_ERR_INVALID;
+    if ((int64_t)((n_tok + 255) / 256) * n_head > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;   // grid size
     if (!std::isfinite(scale)) return MLA_FA_ERR_INVALID;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return MLA_FA_ERR_INVALID;
     if (k_row_stride < (int64_t)n_head * 384 || k_row_stride % 16 || v_row_stride < (int64_t)n_head * 256 ||
         v_row_stride % 16)
         return MLA_FA_ERR_INVALID;
     if (mask) {
-        if (!aligned(mask, 8) || mask_row_stride < 0 || mask_row_stride % 4) return MLA_FA_ERR_INVALID;
+        if (!aligned(mask, 16) || mask_row_stride < 0 || mask_row_stride % 8) return MLA_FA_ERR_INVALID;
         if (n_tok > 1 && mask_row_stride < n_kv) return MLA_FA_ERR_INVALID;
     }
     MhaArgs a;

@@ -33,10 +33,17 @@ __device__ __forceinline__ unsigned f32_to_bf16_bits(float x) {   // nearest eve
     return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats -> two f16 (nearest even) in one register: one v_cvt_pk_f16_f32
 __device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (unsigned)__builtin_bit_cast(unsigned short, a) |
-           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){lo, hi}, f16x2v));
+}
+// two floats -> two bf16 (nearest even) in one register: one v_cvt_pk_bf16_f32
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
 __device__ __forceinline__ float f16_bits_to_f32(unsigned short b) {
@@ -45,7 +52,7 @@ __device__ __forceinline__ float f16_bits_to_f32(unsigned short b) {
 
 template <int KIND> __device__ __forceinline__ unsigned pack_p(float lo, float hi) {
     if constexpr (KIND == KV_BF16)
-        return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+        return pack_bf16x2(lo, hi);
     else
         return pack_f16x2(lo, hi);
 }

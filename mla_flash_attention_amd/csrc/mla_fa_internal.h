@@ -63,7 +63,7 @@ struct MhaArgs {
     int64_t k_row_stride;          // bytes
     int64_t v_row_stride;          // bytes
     const uint16_t *mask;          // f16 bits, token t at mask + t * mask_row_stride, or nullptr
-    int64_t mask_row_stride;       // elements, a multiple of 4 (8-byte mask loads)
+    int64_t mask_row_stride;       // elements, a multiple of 8 (16-byte mask copies)
     float *out;                    // [n_tok][n_head][128] fp32
     int64_t n_kv;
     int n_tok, n_head;

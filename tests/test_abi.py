@@ -168,9 +168,9 @@ def _mha(L, **kw):
     (dict(ks=128 * 384 - 16), B.MLA_FA_ERR_INVALID),                 # key rows overlap
     (dict(vs=128 * 256 + 8), B.MLA_FA_ERR_INVALID),                  # value stride not a multiple of 16
     (dict(k=FAKE + 8), B.MLA_FA_ERR_INVALID),                        # misaligned keys
-    (dict(mask=FAKE + 2, ms=16), B.MLA_FA_ERR_INVALID),              # mask not 8-byte aligned
-    (dict(mask=FAKE, ms=18), B.MLA_FA_ERR_INVALID),                  # mask stride not a multiple of 4
-    (dict(mask=FAKE, ms=12), B.MLA_FA_ERR_INVALID),                  # mask rows shorter than n_kv
+    (dict(mask=FAKE + 8, ms=16), B.MLA_FA_ERR_INVALID),              # mask not 16-byte aligned
+    (dict(mask=FAKE, ms=20), B.MLA_FA_ERR_INVALID),                  # mask stride not a multiple of 8
+    (dict(mask=FAKE, ms=8), B.MLA_FA_ERR_INVALID),                   # mask rows shorter than n_kv
     (dict(scale=float("nan")), B.MLA_FA_ERR_INVALID),
     (dict(qt=B.MLA_FA_F16), B.MLA_FA_ERR_UNSUPPORTED),               # q and cache types differ
     (dict(qt=B.MLA_FA_Q8_0, kvt=B.MLA_FA_Q8_0), B.MLA_FA_ERR_INVALID),

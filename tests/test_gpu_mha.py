@@ -37,7 +37,7 @@ def _padded(a: np.ndarray, width: int):
 
 def run_mha(p, k_pad=0, v_pad=0, mask_pad=None):
     """Run the per-head kernel on problem p; k_pad / v_pad extra elements per key row,
-    mask_pad the mask row stride (None = n_kv rounded up to 4)."""
+    mask_pad the mask row stride (None = n_kv rounded up to 8)."""
     import torch
     from mla_flash_attention_amd import binding as B
     q = to_dev(p.q)
@@ -45,7 +45,7 @@ def run_mha(p, k_pad=0, v_pad=0, mask_pad=None):
     v = _padded(p.v, p.n_head * DV + v_pad) if v_pad else to_dev(p.v)
     mask = None
     if p.mask is not None:
-        ms = mask_pad if mask_pad is not None else (p.n_kv + 3) // 4 * 4
+        ms = mask_pad if mask_pad is not None else (p.n_kv + 7) // 8 * 8
         mask = _padded(p.mask, ms)
     out = torch.full((p.n_tok, p.n_head, DV), float("nan"), dtype=torch.float32, device="cuda")
     B.mla_fa_prefill_mha(q, p.q_type, k, v, p.kv_type, p.scale, out, causal=p.causal, mask=mask)
@@ -74,14 +74,14 @@ def test_mha_dense(n_tok, n_head, n_kv, t, causal, seed):
 
 
 @pytest.mark.parametrize("mask_kind,n_kv,causal,t", [
-    ("random", 333, False, BF16),     # row length not a multiple of 4 (stride padded to 336)
+    ("random", 333, False, BF16),     # row length not a multiple of 8 (stride padded to 336)
     ("runs_bias", 520, True, F16),
     ("random", 256, True, BF16),      # tight stride: mask rows exactly n_kv long
 ])
 def test_mha_masked(mask_kind, n_kv, causal, t):
     n_tok = min(260, n_kv) if causal else 96
     p = synth.make_mha_problem(n_tok, 2, n_kv, t, t, seed=11, causal=causal, mask_kind=mask_kind)
-    got = run_mha(p, mask_pad=n_kv if n_kv % 4 == 0 else None)
+    got = run_mha(p, mask_pad=n_kv if n_kv % 8 == 0 else None)
     assert_parity(got, ref_mha(p), f"mha mask {mask_kind} n_kv={n_kv}")
 
 
