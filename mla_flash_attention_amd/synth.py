@@ -284,3 +284,52 @@ def make_mha_problem(n_tok: int, n_head: int, n_kv: int, q_type: int = TYPE_BF16
     mask = None if mask_kind is None else make_mask(mask_kind, 1, n_tok, n_kv, rng(seed, 2))[0]
     return MhaProblem(q=q, k=k, v=v, q_type=q_type, kv_type=kv_type, n_tok=n_tok, n_head=n_head, n_kv=n_kv,
                       scale=np.float32(DEFAULT_SCALE if scale is None else scale), causal=causal, mask=mask)
+
+
+# ---------------------------------------------------------------- absorbed projections
+QK_NOPE = 128      # per-head query/key dims without RoPE
+QK_ROPE = 64       # RoPE dims (shared key part in the cache row)
+V_HEAD = 128       # per-head value dims
+
+
+@dataclasses.dataclass
+class AbsorbedProblem:
+    """Latent attention with the per-head projections either side (bits):
+    q_nope [n_seq][n_tok][n_head][128], q_pe [..][64], w_uk [n_head][512][128] (latent from
+    key dims), w_uv [n_head][128][512] (value dims from latent), cache as in Problem."""
+    q_nope: np.ndarray
+    q_pe: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    q_type: int
+    kv: np.ndarray
+    kv_type: int
+    n_seq: int
+    n_tok: int
+    n_head: int
+    n_kv: int
+    scale: np.float32
+    causal: bool = False
+    mask: np.ndarray | None = None
+    kv_len: np.ndarray | None = None
+
+
+def make_absorbed_problem(n_seq: int, n_tok: int, n_head: int, n_kv: int, q_type: int = TYPE_BF16,
+                          kv_type: int = TYPE_BF16, seed: int = 0, causal: bool = False,
+                          mask_kind: str | None = None, ragged: bool = False,
+                          scale: float | None = None) -> AbsorbedProblem:
+    """Cache, mask and lengths as make_problem (streams 1, 2, 3); q_nope stream 6, q_pe
+    stream 7, W_UK stream 8 (N(0, 1/128): latent queries of unit variance), W_UV stream 9
+    (N(0, 1/512)); all rounded to q_type.  Scale defaults to 1/sqrt(192), the per-head
+    key width the projections stand for."""
+    base = make_problem(kind="decode", n_seq=n_seq, n_tok=n_tok, n_head=n_head, n_kv=n_kv, q_type=q_type,
+                        kv_type=kv_type, seed=seed, causal=causal, mask_kind=mask_kind, ragged=ragged)
+    qn = rng(seed, 6).standard_normal((n_seq, n_tok, n_head, QK_NOPE), dtype=np.float32)
+    qp = rng(seed, 7).standard_normal((n_seq, n_tok, n_head, QK_ROPE), dtype=np.float32)
+    wk = rng(seed, 8).standard_normal((n_head, DV, QK_NOPE), dtype=np.float32) * np.float32(1 / np.sqrt(QK_NOPE))
+    wv = rng(seed, 9).standard_normal((n_head, V_HEAD, DV), dtype=np.float32) * np.float32(1 / np.sqrt(DV))
+    return AbsorbedProblem(q_nope=round_bits(qn, q_type), q_pe=round_bits(qp, q_type), w_uk=round_bits(wk, q_type),
+                           w_uv=round_bits(wv, q_type), q_type=q_type, kv=base.kv, kv_type=kv_type, n_seq=n_seq,
+                           n_tok=n_tok, n_head=n_head, n_kv=n_kv,
+                           scale=np.float32(1 / np.sqrt(QK_NOPE + QK_ROPE) if scale is None else scale),
+                           causal=causal, mask=base.mask, kv_len=base.kv_len)

@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by 
 CPU-baseline leg of bench.py, never by the product package.  It shares no code with
 the HIP path; both receive the same bytes from the seeded generators.
 
-What each function follows is documented in mla_oracle.c.  Every function here is
-pinned by tests/test_oracle_pins.py; none is "parity unpinned".
+What each function follows is documented in mla_oracle.c and in the docstrings here.
+Every function is pinned (tests/test_oracle_pins.py, test_oracle_ext_pins.py,
+test_oracle_mha_pins.py, test_oracle_absorbed_pins.py); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -48,6 +49,12 @@ def _lib():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
             ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        lib.oracle_mla_attention_q64.restype = ctypes.c_int64
+        lib.oracle_mla_attention_q64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_mha_attention.restype = ctypes.c_int64
         lib.oracle_mha_attention.argtypes = [
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
@@ -145,6 +152,57 @@ def attention_problem(p, rows=None, return_stats=False):
                      return_stats=return_stats, kv_len=getattr(p, "kv_len", None),
                      alibi=getattr(p, "alibi", None), sinks=getattr(p, "sinks", None),
                      softcap=getattr(p, "softcap", 0.0))
+
+
+def absorbed_attention(q_nope, q_pe, q_type, w_uk, w_uv, kv, kv_type, n_seq, n_tok, n_head, n_kv, scale, *,
+                       causal=False, mask=None, rows=None, kv_len=None, return_latent=False):
+    """fp64 MLA attention with the absorbed projections either side, [len(rows) or
+    n_seq*n_tok*n_head][128].
+
+    The per-head up-projection of the latent cache is split into W_UK (128 key dims from
+    the 512 latent) and W_UV (128 value dims from the 512 latent); instead of
+    decompressing every cached row, W_UK is folded into the query and W_UV applied to
+    the attention output ("ik_llama.cpp -mla flag deep-dive": wkv_b split per head into
+    wk_b / wv_b, "128 x 512 x 128"; "Vulkan backend fused Flash Attention: DeepSeek MLA
+    local inference", sections 3.2-3.3 and 6.1: the fused path is logically the
+    step-by-step one).  In order:
+        q_lat[h] = W_UK[h] q_nope[h]                    (512)
+        q[h]     = [q_lat[h], q_pe[h]]                  (576, not rounded)
+        O_lat    = latent attention of q over the cache (512; `attention` above, in fp64)
+        out[h]   = W_UV[h] O_lat[h]                     (128)
+    q_nope uint16 [n_seq][n_tok][n_head][128], q_pe uint16 [..][64] (type q_type);
+    w_uk uint16 [n_head][512][128], w_uv uint16 [n_head][128][512] (type q_type, weights
+    stored output-major like a linear layer); kv as for `attention`.
+    """
+    qn = decode(np.ascontiguousarray(q_nope, dtype=np.uint16), q_type).reshape(n_seq, n_tok, n_head, 128)
+    qp = decode(np.ascontiguousarray(q_pe, dtype=np.uint16), q_type).reshape(n_seq, n_tok, n_head, 64)
+    wk = decode(np.ascontiguousarray(w_uk, dtype=np.uint16), q_type).reshape(n_head, 512, 128)
+    wv = decode(np.ascontiguousarray(w_uv, dtype=np.uint16), q_type).reshape(n_head, 128, 512)
+    q_lat = np.einsum("sthd,hcd->sthc", qn, wk)
+    q64 = np.ascontiguousarray(np.concatenate([q_lat, qp], axis=-1), dtype=np.float64)
+    kv = np.ascontiguousarray(kv)
+    row_bytes = kv.shape[-1] * kv.itemsize
+    assert kv.shape[-2] == n_kv
+    seq_stride = 0 if (kv.shape[0] == 1 and n_seq > 1) else n_kv * row_bytes
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.uint16).reshape(n_seq, n_tok, n_kv)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.size
+    else:
+        n_rows = n_seq * n_tok * n_head
+    if kv_len is not None:
+        kv_len = np.ascontiguousarray(kv_len, dtype=np.int32).reshape(n_seq)
+    o_lat = np.zeros((n_rows, 512), dtype=np.float64)
+    rc = _lib().oracle_mla_attention_q64(
+        _ptr(q64), _ptr(kv), kv_type, row_bytes, seq_stride, n_seq, n_tok, n_head, n_kv, 576, 512,
+        _ptr(kv_len), 1 if causal else 0, _ptr(mask), n_kv, n_tok * n_kv, float(np.float32(scale)),
+        _ptr(rows), n_rows, _ptr(o_lat))
+    if rc < 0:
+        raise ValueError(f"oracle_mla_attention_q64 failed ({rc})")
+    heads = (rows if rows is not None else np.arange(n_rows)) % n_head
+    out = np.einsum("iec,ic->ie", wv[heads], o_lat)
+    return (out, o_lat) if return_latent else out
 
 
 def mha_attention(q, q_type, k, v, kv_type, scale, *, causal=False, mask=None, rows=None):

@@ -145,6 +145,15 @@ int oracle_num_threads(void) {
  *          for a row with neither kept cell nor sink
  * Returns the number of rows with no kept cell, or a negative value on bad input.
  */
+static int64_t attention_core(const uint16_t *q, int q_type, const double *q64, const uint8_t *kv,
+                              int kv_type, int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                              int n_tok, int n_head, int64_t n_kv, int dk, int dv,
+                              const int32_t *kv_len, int causal, const uint16_t *mask,
+                              int64_t mask_tok_stride, int64_t mask_seq_stride,
+                              const double *alibi, const double *sinks, double softcap,
+                              double scale, const int64_t *rows, int64_t n_rows, double *out,
+                              double *row_max, double *row_sum);
+
 int64_t oracle_mla_attention_ext(const uint16_t *q, int q_type, const uint8_t *kv, int kv_type,
                                  int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
                                  int n_tok, int n_head, int64_t n_kv, int dk, int dv,
@@ -153,10 +162,37 @@ int64_t oracle_mla_attention_ext(const uint16_t *q, int q_type, const uint8_t *k
                                  const double *alibi, const double *sinks, double softcap,
                                  double scale, const int64_t *rows, int64_t n_rows, double *out,
                                  double *row_max, double *row_sum) {
-    if (!q || !kv || !out || n_seq < 1 || n_tok < 1 || n_head < 1 || n_kv < 1 || dk < 1 ||
+    if (!q || (q_type != OR_F16 && q_type != OR_BF16)) return -1;
+    return attention_core(q, q_type, NULL, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_tok,
+                          n_head, n_kv, dk, dv, kv_len, causal, mask, mask_tok_stride, mask_seq_stride,
+                          alibi, sinks, softcap, scale, rows, n_rows, out, row_max, row_sum);
+}
+
+/* The same with the queries given in fp64, q64[n_seq][n_tok][n_head][dk] (used where the
+ * query is itself computed, e.g. absorbed from per-head dims; no rounding to 16 bits). */
+int64_t oracle_mla_attention_q64(const double *q64, const uint8_t *kv, int kv_type,
+                                 int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                                 int n_tok, int n_head, int64_t n_kv, int dk, int dv,
+                                 const int32_t *kv_len, int causal, const uint16_t *mask,
+                                 int64_t mask_tok_stride, int64_t mask_seq_stride, double scale,
+                                 const int64_t *rows, int64_t n_rows, double *out) {
+    if (!q64) return -1;
+    return attention_core(NULL, 0, q64, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_tok,
+                          n_head, n_kv, dk, dv, kv_len, causal, mask, mask_tok_stride, mask_seq_stride,
+                          NULL, NULL, 0.0, scale, rows, n_rows, out, NULL, NULL);
+}
+
+static int64_t attention_core(const uint16_t *q, int q_type, const double *q64, const uint8_t *kv,
+                              int kv_type, int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                              int n_tok, int n_head, int64_t n_kv, int dk, int dv,
+                              const int32_t *kv_len, int causal, const uint16_t *mask,
+                              int64_t mask_tok_stride, int64_t mask_seq_stride,
+                              const double *alibi, const double *sinks, double softcap,
+                              double scale, const int64_t *rows, int64_t n_rows, double *out,
+                              double *row_max, double *row_sum) {
+    if (!kv || !out || n_seq < 1 || n_tok < 1 || n_head < 1 || n_kv < 1 || dk < 1 ||
         dv < 1 || dv > dk || softcap < 0.0)
         return -1;
-    if (q_type != OR_F16 && q_type != OR_BF16) return -1;
     if (kv_type == OR_Q8_0 && dk % 32) return -1;
     int64_t total = (int64_t)n_seq * n_tok * n_head;
     if (!rows) n_rows = total;
@@ -191,7 +227,10 @@ int64_t oracle_mla_attention_ext(const uint16_t *q, int q_type, const uint8_t *k
             double *score = (double *)malloc((size_t)(len > 0 ? len : 1) * sizeof(double));
             double *p = (double *)malloc((size_t)(len > 0 ? len : 1) * sizeof(double));
             double *o = out + i * dv;
-            decode_row((const uint8_t *)(q + r * dk), q_type, dk, qv);
+            if (q64)
+                memcpy(qv, q64 + r * dk, (size_t)dk * sizeof(double));
+            else
+                decode_row((const uint8_t *)(q + r * dk), q_type, dk, qv);
 
             /* score_j = cap(scale * q.k_j) + bias_j, or -inf for a cell that is not kept */
             double m = -INFINITY;
