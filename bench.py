@@ -8,7 +8,9 @@ every input already resident in HBM.  Timed steps rotate over 4 copies of the in
 HBM.  Prints one JSON line (see the repository's bench contract).
 
 Secondary lines (same JSON object, key "secondary"): the other workloads - 16-head
-f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells.
+f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells,
+ragged 2-token decode, per-head (DK=192 / DV=128) prefill, and decode with the absorbed
+W_UK / W_UV projections either side.
 """
 from __future__ import annotations
 
@@ -264,6 +266,32 @@ def _time_mha(B, p, steps, warmup):
                 p90=float(np.percentile(ms, 90)))
 
 
+def _time_absorbed(B, p, steps, warmup):
+    """Back-to-back mla_fa_absorbed calls (query projection, attention, merge, output
+    projection) between two events."""
+    import torch
+    stream = torch.cuda.current_stream()
+    qn, qp, wk, wv, kv = _dev(p.q_nope), _dev(p.q_pe), _dev(p.w_uk), _dev(p.w_uv), _dev(p.kv)
+    out = torch.empty((p.n_seq, p.n_tok, p.n_head, 128), dtype=torch.float32, device="cuda")
+    ns = B.mla_fa_auto_splits(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type)
+    ws = B.absorbed_workspace_for(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type, ns)
+
+    def call():
+        B.mla_fa_absorbed(qn, qp, p.q_type, wk, wv, kv, p.kv_type, p.scale, out, causal=p.causal, n_split=ns,
+                          workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return dict(step_ms=t0.elapsed_time(t1) / steps, n_split=ns)
+
+
 def _algo_decode(p, kept=None):
     """Algorithmic bytes and flops of one decode call: cache rows attended, Q, O (and the
     mask/index traffic of the sparse path); flops 2*H*(576+512) per attended cell."""
@@ -360,6 +388,16 @@ def main():
             sec["n2_prefill_mha_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
                                                           cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
                                                           mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
+        if want("n4"):
+            # absorbed projections either side of the decode workload's attention: 4 sequences x
+            # 128 heads over 32768-cell bf16 caches, plus W_UK / W_UV (16 MiB each)
+            p = synth.make_absorbed_problem(4, 1, 128, 32768, synth.TYPE_BF16, synth.TYPE_BF16, seed=2)
+            r = _time_absorbed(B, p, args.steps, args.warmup)
+            cells = p.n_seq * p.n_kv
+            nbytes = cells * 1152 + 2 * p.n_head * 512 * 128 * 2
+            sec["n4_absorbed_decode_4x128h_32768"] = dict(
+                ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3), n_split=r["n_split"],
+                algorithmic_bytes=nbytes, hbm_frac=nbytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
         if want("c4"):
             p = synth.make_config(4)
             r = _time_decode(B, p, args.copies, args.steps, args.warmup)

@@ -206,6 +206,39 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
                        float *out, void *stream);
 
 /*
+ * Latent attention with the absorbed per-head projections either side, from per-head
+ * query parts to per-head outputs.  The per-head up-projection of the latent cache is
+ * split into W_UK (128 key dims from the 512 latent) and W_UV (128 value dims from the
+ * latent); W_UK is folded into the query and W_UV applied to the attention output
+ * instead of decompressing every cached row ("ik_llama.cpp -mla flag deep-dive": wkv_b
+ * split per head into wk_b / wv_b; "Vulkan backend fused Flash Attention: DeepSeek MLA
+ * local inference", sections 3.2-3.3 and 6.1).  For row r = (s, t) and head h:
+ *     q_lat = W_UK[h] q_nope[r][h]                  (512; rounded to q_type on the GPU)
+ *     O     = latent attention of [q_lat, q_pe[r][h]] as mla_fa_attend computes it
+ *     out[r][h] = W_UV[h] O                         (128; O rounded to q_type as the
+ *                                                    MFMA operand, fp32 accumulation)
+ *   q_nope   [n_seq][n_tok][n_head][128], q_pe [n_seq][n_tok][n_head][64]: q_type bits
+ *            (f16 or bf16), device, 16-byte aligned.
+ *   w_uk     [n_head][512][128], w_uv [n_head][128][512]: q_type bits, stored
+ *            output-major (a linear layer's [out][in]), device, 16-byte aligned.
+ *   kv, kv_row_stride, kv_seq_stride, n_kv, kv_len, causal, mask, mask strides, scale:
+ *            as for mla_fa_attend (scale is typically 1/sqrt(192)).
+ *   out      [n_seq][n_tok][n_head][128] fp32, device, 16-byte aligned.
+ *   workspace  device, 256-byte aligned, at least mla_fa_absorbed_workspace_size(
+ *            n_seq*n_tok, n_head, n_kv, kv_type, n_split) bytes: it holds the 576-wide
+ *            queries, the latent outputs and the split partials.
+ * Four launches on `stream`: query projection (with the q_pe copy), attention, merge
+ * (when split), output projection.  Errors as for mla_fa_attend; ERR_WORKSPACE when the
+ * workspace is missing or short.
+ */
+size_t mla_fa_absorbed_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split);
+int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void *w_uk, const void *w_uv,
+                    const void *kv, int kv_type, int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                    int n_tok, int n_head, int64_t n_kv, const int32_t *kv_len, int causal, const uint16_t *mask,
+                    int64_t mask_seq_stride, int64_t mask_tok_stride, float scale, float *out, int n_split,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Sparse-mask index compaction.  For each of n_rows f16 mask rows (row r at
  * mask + r*mask_row_stride elements, n_kv cells), writes the ascending list of cells
  * whose mask is not -inf (bit pattern != 0xFC00) to idx + r*idx_row_stride and its

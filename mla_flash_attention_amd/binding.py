@@ -22,7 +22,8 @@ MLA_FA_OK, MLA_FA_ERR_INVALID, MLA_FA_ERR_UNSUPPORTED, MLA_FA_ERR_WORKSPACE, MLA
 
 EXPORTS = ("mla_fa_strerror", "mla_fa_version", "mla_fa_auto_splits", "mla_fa_workspace_size",
            "mla_fa_decode", "mla_fa_decode_partials", "mla_fa_merge_partials", "mla_fa_prefill",
-           "mla_fa_attend", "mla_fa_prefill_mha", "fa_mask_compact")
+           "mla_fa_attend", "mla_fa_prefill_mha", "mla_fa_absorbed_workspace_size", "mla_fa_absorbed",
+           "fa_mask_compact")
 
 _LIB = None
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -63,6 +64,11 @@ def lib() -> ctypes.CDLL:
         L.mla_fa_attend.restype = _i
         L.mla_fa_attend.argtypes = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64, _i64,
                                     _p, _p, _f, _f, _p, _i, _p, _sz, _p]
+        L.mla_fa_absorbed_workspace_size.restype = _sz
+        L.mla_fa_absorbed_workspace_size.argtypes = [_i, _i, _i64, _i, _i]
+        L.mla_fa_absorbed.restype = _i
+        L.mla_fa_absorbed.argtypes = [_p, _p, _i, _p, _p, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64,
+                                      _i64, _f, _p, _i, _p, _sz, _p]
         L.mla_fa_prefill_mha.restype = _i
         L.mla_fa_prefill_mha.argtypes = [_p, _i, _p, _p, _i, _i64, _i64, _i, _i, _i64, _i, _p, _i64, _f, _p, _p]
         _LIB = L
@@ -196,6 +202,35 @@ def mla_fa_prefill_mha(q, q_type, k, v, kv_type, scale, out, *, causal=True, mas
                                     _ptr(mask), 0 if mask is None else mask.stride(0), float(scale), _ptr(out),
                                     _stream(stream)),
            "mla_fa_prefill_mha")
+    return out
+
+
+def mla_fa_absorbed_workspace_size(n_rows: int, n_head: int, n_kv: int, kv_type: int, n_split: int = 0) -> int:
+    return int(lib().mla_fa_absorbed_workspace_size(n_rows, n_head, n_kv, kv_type, n_split))
+
+
+def absorbed_workspace_for(n_rows, n_head, n_kv, kv_type, n_split=0, device="cuda"):
+    nbytes = mla_fa_absorbed_workspace_size(n_rows, n_head, n_kv, kv_type, n_split)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def mla_fa_absorbed(q_nope, q_pe, q_type, w_uk, w_uv, kv, kv_type, scale, out, *, kv_len=None, causal=False,
+                    mask=None, n_split=0, workspace=None, stream=None):
+    """q_nope [n_seq][n_tok][n_head][128], q_pe [..][64] (16-bit bits), w_uk [n_head][512][128],
+    w_uv [n_head][128][512] (same type), kv [n_seq][n_kv][row], out fp32 [n_seq][n_tok][n_head][128];
+    kv_len int32 [n_seq]; mask [n_seq][n_tok][>=n_kv] f16 bits."""
+    n_seq, n_tok, n_head = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+    n_kv = kv.shape[-2]
+    if workspace is None:
+        workspace = absorbed_workspace_for(n_seq * n_tok, n_head, n_kv, kv_type, n_split, device=q_nope.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    mseq = 0 if mask is None else mask.stride(0)
+    mtok = 0 if mask is None else mask.stride(1)
+    _check(lib().mla_fa_absorbed(_ptr(q_nope), _ptr(q_pe), q_type, _ptr(w_uk), _ptr(w_uv), _ptr(kv), kv_type,
+                                 _row_stride_bytes(kv), _seq_stride_bytes(kv, n_seq), n_seq, n_tok, n_head, n_kv,
+                                 _ptr(kv_len), 1 if causal else 0, _ptr(mask), mseq, mtok, float(scale), _ptr(out),
+                                 n_split, _ptr(workspace), ws_bytes, _stream(stream)),
+           "mla_fa_absorbed")
     return out
 
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmlafa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["attn.hip", "mha.hip", "compact.hip", "api.hip"]
+SOURCES = ["attn.hip", "mha.hip", "proj.hip", "compact.hip", "api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

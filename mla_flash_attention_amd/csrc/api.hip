@@ -230,6 +230,21 @@ Common decode_common(const void *q, int q_type, const void *kv, int kv_type, int
     return c;
 }
 
+// Workspace of mla_fa_absorbed: the 576-wide queries (16-bit), the latent outputs (fp32)
+// and the split partials, each section 256-byte aligned.
+struct AbsorbedLayout {
+    size_t q_off, o_off, part_off, total;
+};
+AbsorbedLayout absorbed_layout(int64_t n_rows, int n_head, int n_split) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    AbsorbedLayout l;
+    l.q_off = 0;
+    l.o_off = up((size_t)n_rows * n_head * kDK * 2);
+    l.part_off = l.o_off + up((size_t)n_rows * n_head * kDV * sizeof(float));
+    l.total = l.part_off + (n_split > 1 ? partial_bytes(n_rows, n_head, n_split) : 0);
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -387,6 +402,70 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
     a.scale_log2 = scale * 1.4426950408889634f;
     hipError_t e = launch_mha(a, kv_kind_of(kv_type), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
+size_t mla_fa_absorbed_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split) {
+    if (n_rows < 1 || n_kv < 1 || check_heads(n_head) || n_split < 0 || n_split > kMaxSplits) return 0;
+    Plan p = make_plan(n_rows, n_head, n_kv, kv_type, n_split);
+    return absorbed_layout(n_rows, n_head, p.n_split).total;
+}
+
+int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void *w_uk, const void *w_uv,
+                    const void *kv, int kv_type, int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq,
+                    int n_tok, int n_head, int64_t n_kv, const int32_t *kv_len, int causal, const uint16_t *mask,
+                    int64_t mask_seq_stride, int64_t mask_tok_stride, float scale, float *out, int n_split,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q_nope || !q_pe || !w_uk || !w_uv || !out) return MLA_FA_ERR_INVALID;
+    if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
+        !aligned(out, 16) || !aligned(workspace, 256))
+        return MLA_FA_ERR_INVALID;
+    if (n_seq < 1 || n_tok < 1 || (int64_t)n_seq * n_tok > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
+    const int64_t n_rows = (int64_t)n_seq * n_tok;
+    int st = check_heads(n_head);
+    if (st) return st;
+    if (n_split < 0 || n_split > kMaxSplits || n_kv < 1) return MLA_FA_ERR_INVALID;
+    const Plan p = make_plan(n_rows, n_head, n_kv, kv_type, n_split);
+    const AbsorbedLayout lay = absorbed_layout(n_rows, n_head, p.n_split);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    // the attention part, on the queries the first projection writes into the workspace
+    Common c;
+    c.q = ws ? ws + lay.q_off : nullptr; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
+    c.kv_row_stride = kv_row_stride; c.kv_seq_stride = kv_seq_stride;
+    c.n_seq = n_seq; c.n_tok = n_tok; c.n_head = n_head; c.n_kv = n_kv; c.causal = causal;
+    c.mask = mask; c.mask_seq_stride = mask_seq_stride; c.mask_tok_stride = mask_tok_stride;
+    c.kv_idx = nullptr; c.kv_idx_count = nullptr; c.idx_seq_stride = 0;
+    c.scale = scale; c.out = ws ? reinterpret_cast<float *>(ws + lay.o_off) : nullptr; c.n_split = p.n_split;
+    c.ws = ws ? ws + lay.part_off : nullptr; c.ws_bytes = lay.total - lay.part_off;
+    c.kv_len = kv_len;
+    if (!workspace || workspace_bytes < lay.total) {
+        // report argument errors first: validate with stand-in buffers
+        Common v = c;
+        v.q = q_nope; v.out = out;
+        st = validate(v);
+        return st ? st : MLA_FA_ERR_WORKSPACE;
+    }
+    st = validate(c);
+    if (st) return st;
+    const int kind = q_type == MLA_FA_BF16 ? KV_BF16 : KV_F16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ProjArgs qa;
+    qa.a = q_nope; qa.a_rs = (int64_t)n_head * 128; qa.a_hs = 128;
+    qa.w = static_cast<const uint16_t *>(w_uk);
+    qa.c = ws + lay.q_off; qa.c_rs = (int64_t)n_head * kDK; qa.c_hs = kDK;
+    qa.extra = static_cast<const uint16_t *>(q_pe); qa.extra_rs = (int64_t)n_head * 64; qa.extra_hs = 64;
+    qa.M = (int)n_rows; qa.N = kDV; qa.K = 128; qa.H = n_head;
+    if (launch_proj(qa, kind, false, false, s) != hipSuccess) return MLA_FA_ERR_HIP;
+    st = run_partials(c, p, s);
+    if (st) return st;
+    st = run_merge(n_rows, n_head, p.n_split, c.out, c.ws, c.ws_bytes, s);
+    if (st) return st;
+    ProjArgs oa;
+    oa.a = c.out; oa.a_rs = (int64_t)n_head * kDV; oa.a_hs = kDV;
+    oa.w = static_cast<const uint16_t *>(w_uv);
+    oa.c = out; oa.c_rs = (int64_t)n_head * 128; oa.c_hs = 128;
+    oa.extra = nullptr; oa.extra_rs = 0; oa.extra_hs = 0;
+    oa.M = (int)n_rows; oa.N = 128; oa.K = kDV; oa.H = n_head;
+    return launch_proj(oa, kind, true, true, s) == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
 int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,

@@ -71,7 +71,24 @@ struct MhaArgs {
     float scale_log2;              // scale * log2(e)
 };
 
+// Per-head product C[r][h] = A[r][h] . W[h]^T (W output-major, 16-bit, same type as the
+// MFMA): element (r, h, k) of A at a + r*a_rs + h*a_hs + k, W[h][n][k] at
+// w + (h*N + n)*K + k, C (r, h, n) at c + r*c_rs + h*c_hs + n (all in elements); A and C
+// 16-bit or fp32.  With `extra`, the 16-bit row part (r, h) at extra + r*extra_rs +
+// h*extra_hs (64 elements) is copied to C columns N .. N + 63.
+struct ProjArgs {
+    const void *a;
+    int64_t a_rs, a_hs;
+    const uint16_t *w;
+    void *c;
+    int64_t c_rs, c_hs;
+    const uint16_t *extra;
+    int64_t extra_rs, extra_hs;
+    int M, N, K, H;
+};
+
 hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);
+hipError_t launch_proj(const ProjArgs &p, int kind, bool a_f32, bool c_f32, hipStream_t stream);
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
                         const float *sinks, hipStream_t stream);
 hipError_t launch_mha(const MhaArgs &a, int kv_kind, hipStream_t stream);

@@ -1,0 +1,226 @@
+// proj.hip -- the per-head projections either side of absorbed MLA attention (gfx950).
+//
+// The per-head up-projection of the latent cache is split into W_UK (key dims from the
+// 512 latent) and W_UV (value dims from the latent); rather than decompressing every
+// cached row, W_UK is folded into the query and W_UV applied to the attention output
+// ("ik_llama.cpp -mla flag deep-dive": wkv_b split per head into wk_b / wv_b; "Vulkan
+// backend fused Flash Attention: DeepSeek MLA local inference", sections 3.2-3.3).  Both
+// are per-head products C[r][h] = A[r][h] . W[h]^T with W stored output-major (a linear
+// layer's [out][in]), so both MFMA operands are contiguous along the reduction:
+//   query side:  q[r][h][0:512] = W_UK[h] q_nope[r][h]   (K = 128, N = 512), written as
+//                16-bit values straight into the 576-wide query rows the attention
+//                kernel reads, with q_pe copied into columns 512..575;
+//   output side: out[r][h] = W_UV[h] O[r][h]             (K = 512, N = 128), O the fp32
+//                latent attention output, rounded to 16 bits as the MFMA operand.
+//
+// A workgroup (4 waves) computes a 64-row x 128-column tile of one head; wave (wr, wc)
+// the 32 x 64 sub-tile at rows 32 wr, columns 64 wc: 2 x 4 blocks of 16x16x32 MFMAs per
+// 32-wide reduction step.  Operands are loaded straight from global memory into MFMA
+// layout (lane: row or column l % 16, reduction elements 8 (l / 16) .. + 7, one 16-byte
+// load), one step ahead of the MFMAs.  These products are small beside the attention
+// (decode: bound by the 16 MB of weights per side; prefill: ~2% of the attention flops),
+// so the kernel stays simple.
+#include "mla_fa_internal.h"
+
+namespace mlafa {
+namespace {
+
+#include "device_common.h"
+
+constexpr int kPRows = 64, kPCols = 128;        // workgroup tile
+
+template <int KIND, bool A_F32>
+__device__ __forceinline__ u32x4 load_a(const ProjArgs &p, int row, int h, int k) {
+    if constexpr (A_F32) {
+        const float *src = static_cast<const float *>(p.a) + (int64_t)row * p.a_rs + (int64_t)h * p.a_hs + k;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(src + 4);
+        return u32x4{pack_p<KIND>(lo[0], lo[1]), pack_p<KIND>(lo[2], lo[3]), pack_p<KIND>(hi[0], hi[1]),
+                     pack_p<KIND>(hi[2], hi[3])};
+    } else {
+        const uint16_t *src = static_cast<const uint16_t *>(p.a) + (int64_t)row * p.a_rs + (int64_t)h * p.a_hs + k;
+        return *reinterpret_cast<const u32x4 *>(src);
+    }
+}
+
+template <int KIND, bool A_F32, bool C_F32>
+__global__ void __launch_bounds__(256) proj_kernel(ProjArgs p) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int h = blockIdx.y;
+    const int n_ct = p.N / kPCols;
+    const int mt = blockIdx.x / n_ct, nt = blockIdx.x % n_ct;
+    const int row0 = mt * kPRows + 32 * (wave & 1);
+    const int col0 = nt * kPCols + 64 * (wave >> 1);
+
+    // this lane's operand rows / columns (rows past M re-read row M - 1 and are not stored)
+    int arow[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = row0 + 16 * rb + l16;
+        arow[rb] = r < p.M ? r : p.M - 1;
+    }
+    const uint16_t *wrow[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wrow[cb] = p.w + ((int64_t)h * p.N + col0 + 16 * cb + l16) * p.K + 8 * g;
+
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 av[2][2], bv[2][4];                     // [buffer][block]
+    auto load = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) av[buf][rb] = load_a<KIND, A_F32>(p, arow[rb], h, 32 * ks + 8 * g);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) bv[buf][cb] = *reinterpret_cast<const u32x4 *>(wrow[cb] + 32 * ks);
+    };
+    const int n_ks = p.K / 32;
+    load(0, 0);
+    for (int ks = 0; ks < n_ks; ks += 2) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int kk = ks + half;
+            if (kk + 1 < n_ks) load(kk + 1, half ^ 1);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[rb][cb] = mfma16x16x32<KIND>(av[half][rb], bv[half][cb], acc[rb][cb]);
+        }
+    }
+
+    // C element (row 16 rb + 4 g + r, column 16 cb + l16) of the wave's sub-tile
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = row0 + 16 * rb + 4 * g + r;
+            if (row >= p.M) continue;
+            const int64_t base = (int64_t)row * p.c_rs + (int64_t)h * p.c_hs + col0 + l16;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                if constexpr (C_F32) {
+                    static_cast<float *>(p.c)[base + 16 * cb] = acc[rb][cb][r];
+                } else {
+                    const unsigned pk = pack_p<KIND>(acc[rb][cb][r], 0.f);
+                    static_cast<uint16_t *>(p.c)[base + 16 * cb] = (uint16_t)(pk & 0xFFFFu);
+                }
+            }
+        }
+
+    // the RoPE part of the query, copied next to the projected part (first column tile)
+    if (p.extra && nt == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = threadIdx.x + 256 * i;          // 64 rows x 8 chunks of 16 bytes
+            const int row = mt * kPRows + (q >> 3), part = q & 7;
+            if (row < p.M) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(p.extra + (int64_t)row * p.extra_rs +
+                                                                 (int64_t)h * p.extra_hs + 8 * part);
+                *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.c) + (int64_t)row * p.c_rs +
+                                           (int64_t)h * p.c_hs + p.N + 8 * part) = v;
+            }
+        }
+    }
+}
+
+// Few rows (decode: M <= 16): the product is bound by reading W, and a 64-row tile would
+// leave most workgroups walking K one load round trip at a time.  A workgroup here takes
+// 16 rows x 64 columns of one head and its four waves split K into quarters, each loading
+// its whole quarter (at most 4 steps of 32) before the MFMAs, then the four partial tiles
+// are summed through LDS.
+constexpr int kSRows = 16, kSCols = 64, kSMaxSteps = 4;
+
+template <int KIND, bool A_F32, bool C_F32>
+__global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs p) {
+    __shared__ float red[4][4][4][64];            // [wave][column block][register][lane]
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int h = blockIdx.y;
+    const int n_ct = p.N / kSCols;
+    const int mt = blockIdx.x / n_ct, nt = blockIdx.x % n_ct;
+    const int col0 = nt * kSCols;
+    const int r_ = mt * kSRows + l16;
+    const int arow = r_ < p.M ? r_ : p.M - 1;
+    const int kq = p.K / 4, steps = kq / 32;      // this wave's K quarter
+    const int k0 = wave * kq;
+
+    u32x4 av[kSMaxSteps], bv[kSMaxSteps][4];
+#pragma unroll
+    for (int s = 0; s < kSMaxSteps; ++s) {
+        if (s < steps) {
+            const int k = k0 + 32 * s + 8 * g;
+            av[s] = load_a<KIND, A_F32>(p, arow, h, k);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                bv[s][cb] = *reinterpret_cast<const u32x4 *>(p.w + ((int64_t)h * p.N + col0 + 16 * cb + l16) * p.K + k);
+        }
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSMaxSteps; ++s)
+        if (s < steps)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc[cb] = mfma16x16x32<KIND>(av[s], bv[s][cb], acc[cb]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][cb][r][lane] = acc[cb][r];
+    __syncthreads();
+    // thread t sums column block t / 64's four registers over the four waves
+    const int cb = threadIdx.x >> 6;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float v = red[0][cb][r][lane] + red[1][cb][r][lane] + red[2][cb][r][lane] + red[3][cb][r][lane];
+        const int row = mt * kSRows + 4 * g + r;
+        if (row < p.M) {
+            const int64_t o = (int64_t)row * p.c_rs + (int64_t)h * p.c_hs + col0 + 16 * cb + l16;
+            if constexpr (C_F32)
+                static_cast<float *>(p.c)[o] = v;
+            else
+                static_cast<uint16_t *>(p.c)[o] = (uint16_t)(pack_p<KIND>(v, 0.f) & 0xFFFFu);
+        }
+    }
+    // the RoPE part of the query (first column tile): 16 rows x 8 chunks of 16 bytes
+    if (p.extra && nt == 0 && threadIdx.x < kSRows * 8) {
+        const int row = mt * kSRows + (threadIdx.x >> 3), part = threadIdx.x & 7;
+        if (row < p.M) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(p.extra + (int64_t)row * p.extra_rs +
+                                                             (int64_t)h * p.extra_hs + 8 * part);
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.c) + (int64_t)row * p.c_rs + (int64_t)h * p.c_hs +
+                                       p.N + 8 * part) = v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_proj(const ProjArgs &p, int kind, bool a_f32, bool c_f32, hipStream_t stream) {
+    if (p.M < 1 || p.H < 1 || p.N % kPCols || p.K % 128 || p.K > 4 * 32 * kSMaxSteps) return hipErrorInvalidValue;
+    const bool skinny = p.M <= kSRows;
+    const dim3 grid(skinny ? (unsigned)(p.N / kSCols)
+                           : (unsigned)((p.M + kPRows - 1) / kPRows) * (unsigned)(p.N / kPCols),
+                    (unsigned)p.H);
+    void (*kern)(ProjArgs) = nullptr;
+#define MLAFA_PROJ_PICK(K_, AF, CF) kern = skinny ? proj_skinny_kernel<K_, AF, CF> : proj_kernel<K_, AF, CF>
+    if (kind == KV_BF16) {
+        if (!a_f32 && !c_f32) MLAFA_PROJ_PICK(KV_BF16, false, false);
+        else if (a_f32 && c_f32) MLAFA_PROJ_PICK(KV_BF16, true, true);
+    } else if (kind == KV_F16) {
+        if (!a_f32 && !c_f32) MLAFA_PROJ_PICK(KV_F16, false, false);
+        else if (a_f32 && c_f32) MLAFA_PROJ_PICK(KV_F16, true, true);
+    }
+#undef MLAFA_PROJ_PICK
+    if (!kern) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace mlafa

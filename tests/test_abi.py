@@ -178,3 +178,38 @@ def _mha(L, **kw):
 ])
 def test_prefill_mha_validation(L, kw, status):
     assert _mha(L, **kw) == status
+
+
+def _absorbed(L, **kw):
+    a = dict(qn=FAKE, qp=FAKE, qt=B.MLA_FA_BF16, wk=FAKE, wv=FAKE, kv=FAKE, kvt=B.MLA_FA_BF16, rs=1152, ss=1152 * 64,
+             n_seq=2, n_tok=1, H=128, n_kv=64, kv_len=None, causal=0, mask=None, ms=0, mt=0, scale=0.1, out=FAKE,
+             n_split=1, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.mla_fa_absorbed(a["qn"], a["qp"], a["qt"], a["wk"], a["wv"], a["kv"], a["kvt"], a["rs"], a["ss"],
+                             a["n_seq"], a["n_tok"], a["H"], a["n_kv"], a["kv_len"], a["causal"], a["mask"], a["ms"],
+                             a["mt"], ctypes.c_float(a["scale"]), a["out"], a["n_split"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qn=None), B.MLA_FA_ERR_INVALID),
+    (dict(qp=None), B.MLA_FA_ERR_INVALID),
+    (dict(wk=None), B.MLA_FA_ERR_INVALID),
+    (dict(wv=FAKE + 8), B.MLA_FA_ERR_INVALID),                       # misaligned weights
+    (dict(ws=FAKE + 16), B.MLA_FA_ERR_INVALID),                      # workspace not 256-byte aligned
+    (dict(n_tok=0), B.MLA_FA_ERR_INVALID),
+    (dict(H=120), B.MLA_FA_ERR_UNSUPPORTED),
+    (dict(qt=B.MLA_FA_F16), B.MLA_FA_ERR_UNSUPPORTED),               # query and cache types differ
+    (dict(causal=1, n_tok=65), B.MLA_FA_ERR_INVALID),
+    (dict(ws=None, wsb=0), B.MLA_FA_ERR_WORKSPACE),
+    (dict(wsb=1024), B.MLA_FA_ERR_WORKSPACE),
+    (dict(ws=None, wsb=0, qn=None), B.MLA_FA_ERR_INVALID),           # argument errors come first
+])
+def test_absorbed_validation(L, kw, status):
+    assert _absorbed(L, **kw) == status
+
+
+def test_absorbed_workspace_size(L):
+    n = L.mla_fa_absorbed_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 1)
+    assert n >= 4 * 128 * (576 * 2 + 512 * 4)
+    assert L.mla_fa_absorbed_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 8) > n    # plus the partials
+    assert L.mla_fa_absorbed_workspace_size(0, 128, 32768, B.MLA_FA_BF16, 1) == 0
