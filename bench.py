@@ -95,7 +95,7 @@ def _dev(a):
 
 def _source_hash():
     h = hashlib.sha256()
-    for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h"):
+    for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
         with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
