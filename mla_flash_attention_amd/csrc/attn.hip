@@ -312,17 +312,25 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // once to f16.  Blocks are 2-byte aligned; 9 dwords cover one at either phase
     // (the last block of the last row ends exactly at the end of the raw stage).
     auto dequant_tile = [&](const unsigned char *raw, unsigned char *f16tile) __attribute__((always_inline)) {
+        // Lane l converts row l, wave w blocks w, w + NW, ...: the lanes of one read are a
+        // row (612 B = 153 dwords, odd mod 64 banks) apart, so every read is conflict-free.
+        // A code c becomes u = c + 128 (flip the sign bit); one v_perm builds the f16 pair
+        // (1024 + u0, 1024 + u1), and (x - 1152) * d in packed f16 gives (c0 d, c1 d): the
+        // subtraction is exact and the product is rounded once, as code * d to f16 is.
+#pragma clang fp contract(off)
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         const unsigned *rw = reinterpret_cast<const unsigned *>(raw);
+        const int r = threadIdx.x & 63;
 #pragma unroll 1
-        for (int task = threadIdx.x; task < kTileKeys * 18; task += NW * 64) {
-            const int r = task / 18, b = task - (task / 18) * 18;
+        for (int b = threadIdx.x >> 6; b < 18; b += NW) {
             const int byte0 = r * kQ8RowBytes + 34 * b;
             const bool odd = (byte0 & 2) != 0;                       // block starts mid-dword
             unsigned w[9];
 #pragma unroll
             for (int i = 0; i < 9; ++i) w[i] = rw[(byte0 >> 2) + i];
-            const float d = f16_bits_to_f32((unsigned short)(odd ? (w[0] >> 16) : (w[0] & 0xFFFFu)));
-            const float nd = -128.f * d;
+            const unsigned dbits = odd ? (w[0] >> 16) : (w[0] & 0xFFFFu);
+            const h2 dd = __builtin_bit_cast(h2, dbits | (dbits << 16));
+            const h2 off = h2{(_Float16)1152.f, (_Float16)1152.f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {                                // 8 values -> 16 B chunk
                 unsigned pk[4];
@@ -331,8 +339,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     const int i = 2 * c + h;                             // code dword i of the block
                     const unsigned code = odd ? w[i + 1] : __builtin_amdgcn_alignbyte(w[i + 1], w[i], 2);
                     const unsigned u = code ^ 0x80808080u;               // code + 128 per byte
-                    pk[2 * h] = pack_f16x2(fmaf((float)(u & 0xFFu), d, nd), fmaf((float)((u >> 8) & 0xFFu), d, nd));
-                    pk[2 * h + 1] = pack_f16x2(fmaf((float)((u >> 16) & 0xFFu), d, nd), fmaf((float)(u >> 24), d, nd));
+                    const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00050004u));
+                    const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00070006u));
+                    pk[2 * h] = __builtin_bit_cast(unsigned, (h2)((x01 - off) * dd));
+                    pk[2 * h + 1] = __builtin_bit_cast(unsigned, (h2)((x23 - off) * dd));
                 }
                 const int lc = 4 * b + c;                                // 16-byte chunk of the row
                 unsigned char *dp = lc < 64 ? f16tile + r * kVRow + 16 * lc
