@@ -11,7 +11,8 @@
 //                16-bit values straight into the 576-wide query rows the attention
 //                kernel reads, with q_pe copied into columns 512..575;
 //   output side: out[r][h] = W_UV[h] O[r][h]             (K = 512, N = 128), O the fp32
-//                latent attention output, rounded to 16 bits as the MFMA operand.
+//                latent attention output, split into a 16-bit head and a 16-bit
+//                remainder, each an MFMA operand (two MFMAs per block).
 //
 // A workgroup (4 waves) computes a 64-row x 128-column tile of one head; wave (wr, wc)
 // the 32 x 64 sub-tile at rows 32 wr, columns 64 wc: 2 x 4 blocks of 16x16x32 MFMAs per
@@ -29,17 +30,35 @@ namespace {
 
 constexpr int kPRows = 64, kPCols = 128;        // workgroup tile
 
+// 16-bit value back to fp32 (exact)
+template <int KIND> __device__ __forceinline__ float unpack_lo(unsigned v) {
+    if constexpr (KIND == KV_BF16)
+        return bf16_bits_to_f32(v & 0xFFFFu);
+    else
+        return f16_bits_to_f32((unsigned short)(v & 0xFFFFu));
+}
+
+// A operand, 8 reduction elements.  16-bit A is loaded as is.  An fp32 A is split into a
+// 16-bit head and the 16-bit rounding of its remainder (a = hi + lo to ~16 significant
+// bits), both used as MFMA operands, so the product is not limited by one 16-bit rounding
+// of A.
 template <int KIND, bool A_F32>
-__device__ __forceinline__ u32x4 load_a(const ProjArgs &p, int row, int h, int k) {
+__device__ __forceinline__ void load_a(const ProjArgs &p, int row, int h, int k, u32x4 &hi, u32x4 &lo) {
     if constexpr (A_F32) {
         const float *src = static_cast<const float *>(p.a) + (int64_t)row * p.a_rs + (int64_t)h * p.a_hs + k;
-        const f32x4 lo = *reinterpret_cast<const f32x4 *>(src);
-        const f32x4 hi = *reinterpret_cast<const f32x4 *>(src + 4);
-        return u32x4{pack_p<KIND>(lo[0], lo[1]), pack_p<KIND>(lo[2], lo[3]), pack_p<KIND>(hi[0], hi[1]),
-                     pack_p<KIND>(hi[2], hi[3])};
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned ph = pack_p<KIND>(x[2 * j], x[2 * j + 1]);
+            hi[j] = ph;
+            lo[j] = pack_p<KIND>(x[2 * j] - unpack_lo<KIND>(ph), x[2 * j + 1] - unpack_lo<KIND>(ph >> 16));
+        }
     } else {
         const uint16_t *src = static_cast<const uint16_t *>(p.a) + (int64_t)row * p.a_rs + (int64_t)h * p.a_hs + k;
-        return *reinterpret_cast<const u32x4 *>(src);
+        hi = *reinterpret_cast<const u32x4 *>(src);
+        lo = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -71,10 +90,10 @@ __global__ void __launch_bounds__(256) proj_kernel(ProjArgs p) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 av[2][2], bv[2][4];                     // [buffer][block]
+    u32x4 av[2][2], al[2][2], bv[2][4];           // [buffer][block]
     auto load = [&](int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) av[buf][rb] = load_a<KIND, A_F32>(p, arow[rb], h, 32 * ks + 8 * g);
+        for (int rb = 0; rb < 2; ++rb) load_a<KIND, A_F32>(p, arow[rb], h, 32 * ks + 8 * g, av[buf][rb], al[buf][rb]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) bv[buf][cb] = *reinterpret_cast<const u32x4 *>(wrow[cb] + 32 * ks);
     };
@@ -88,8 +107,10 @@ __global__ void __launch_bounds__(256) proj_kernel(ProjArgs p) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
+                for (int cb = 0; cb < 4; ++cb) {
                     acc[rb][cb] = mfma16x16x32<KIND>(av[half][rb], bv[half][cb], acc[rb][cb]);
+                    if constexpr (A_F32) acc[rb][cb] = mfma16x16x32<KIND>(al[half][rb], bv[half][cb], acc[rb][cb]);
+                }
         }
     }
 
@@ -150,12 +171,12 @@ __global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs p) {
     const int kq = p.K / 4, steps = kq / 32;      // this wave's K quarter
     const int k0 = wave * kq;
 
-    u32x4 av[kSMaxSteps], bv[kSMaxSteps][4];
+    u32x4 av[kSMaxSteps], al[kSMaxSteps], bv[kSMaxSteps][4];
 #pragma unroll
     for (int s = 0; s < kSMaxSteps; ++s) {
         if (s < steps) {
             const int k = k0 + 32 * s + 8 * g;
-            av[s] = load_a<KIND, A_F32>(p, arow, h, k);
+            load_a<KIND, A_F32>(p, arow, h, k, av[s], al[s]);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
                 bv[s][cb] = *reinterpret_cast<const u32x4 *>(p.w + ((int64_t)h * p.N + col0 + 16 * cb + l16) * p.K + k);
@@ -168,7 +189,10 @@ __global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs p) {
     for (int s = 0; s < kSMaxSteps; ++s)
         if (s < steps)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) acc[cb] = mfma16x16x32<KIND>(av[s], bv[s][cb], acc[cb]);
+            for (int cb = 0; cb < 4; ++cb) {
+                acc[cb] = mfma16x16x32<KIND>(av[s], bv[s][cb], acc[cb]);
+                if constexpr (A_F32) acc[cb] = mfma16x16x32<KIND>(al[s], bv[s][cb], acc[cb]);
+            }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
