@@ -9,7 +9,9 @@
 // walking the row in 1024-cell chunks with a workgroup scan per chunk) is not used.
 //
 // gfx950 specifics: one workgroup of 16 wave64s per row; each lane loads 16 bytes
-// (8 cells) per step, so a wave covers 512 consecutive cells per load.  Per-lane kept
+// (8 cells) per step, so a wave covers 512 consecutive cells per load, and whole batches
+// of 8 steps issue their 8 loads back to back before any is used (a row's segments are
+// otherwise walked one memory round trip per step).  Per-lane kept
 // counts (0..8) are prefix-summed across the wave with four ballots (one per count
 // bit) and mbcnt, so the scan inside a wave costs no LDS.  The only LDS traffic is
 // the 16 segment counts.  Rows whose base is not 16-byte aligned take a one-cell-per-
@@ -71,9 +73,27 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     const int64_t s0 = (int64_t)wave * seg;
     const int64_t s1 = s0 + seg < n_kv ? s0 + seg : n_kv;
 
-    // pass 1: count this segment's kept cells
+    // pass 1: count this segment's kept cells (whole batches of kBatch steps first)
+    constexpr int kBatch = 8;
     unsigned my_total = 0;
-    for (int64_t b = s0; b < s1; b += step) {
+    int64_t b = s0;
+    if (vec) {
+        for (; b + kBatch * 512 <= s1; b += kBatch * 512) {
+            u16x8 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const u16x8 *>(row + b + 512 * u + 8 * lane);
+            unsigned c = 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) c += (unsigned)(v[u][e] != kNegInf);
+            // c <= 64: the wave total by ballots over its 7 bits
+#pragma unroll
+            for (int bit = 0; bit < 7; ++bit)
+                my_total += (unsigned)__builtin_popcountll(__builtin_amdgcn_ballot_w64((c >> bit) & 1u)) << bit;
+        }
+    }
+    for (; b < s1; b += step) {
         if (vec) {
             const unsigned k = kept_bits8(row, b + 8 * lane, s1);
             unsigned below, tot;
@@ -96,8 +116,32 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     }
     if (threadIdx.x == 0) count[blockIdx.x] = (int32_t)all;
 
-    // pass 2: write this segment's kept cells, ascending
-    for (int64_t b = s0; b < s1; b += step) {
+    // pass 2: write this segment's kept cells, ascending (whole batches first)
+    b = s0;
+    if (vec) {
+        for (; b + kBatch * 512 <= s1; b += kBatch * 512) {
+            u16x8 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const u16x8 *>(row + b + 512 * u + 8 * lane);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t base = b + 512 * u + 8 * lane;
+                unsigned k = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) k |= (unsigned)(v[u][e] != kNegInf) << e;
+                unsigned below, tot;
+                wave_scan4(__builtin_popcount(k), below, tot);
+                unsigned pos = offset + below;
+                while (k) {
+                    const int e = __builtin_ctz(k);
+                    out[pos++] = (int32_t)(base + e);
+                    k &= k - 1;
+                }
+                offset += tot;
+            }
+        }
+    }
+    for (; b < s1; b += step) {
         if (vec) {
             const int64_t base = b + 8 * lane;
             unsigned k = kept_bits8(row, base, s1);
