@@ -11,6 +11,10 @@ Secondary lines (same JSON object, key "secondary"): the other workloads - 16-he
 f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells,
 ragged 2-token decode, per-head (DK=192 / DV=128) prefill, and decode with the absorbed
 W_UK / W_UV projections either side.
+
+Key "measured_peaks": what this GPU measurably delivers (HBM stream read, dense bf16
+MFMA issue, LDS reads; include/mla_peaks.h), so each roofline fraction is also stated
+against a measured peak ("frac_measured", "mfma_frac_measured") beside the published one.
 """
 from __future__ import annotations
 
@@ -41,6 +45,7 @@ def _args():
     ap.add_argument("--copies", type=int, default=4, help="rotating input copies (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak micro-benchmarks")
     ap.add_argument("--only", default="", help="run only these workloads, e.g. 'c2' or 'c3,c4'")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
@@ -307,6 +312,45 @@ def _algo_decode(p, kept=None):
     return cells, kernel_bytes, call_bytes, flops
 
 
+def _measured_peaks(torch, reps=5):
+    """What this GPU measurably delivers (libmlapeaks, include/mla_peaks.h): HBM stream
+    read of 4 GiB (past the 256 MB last-level cache), dense bf16 MFMA issue, and LDS
+    reads (ds_read_b128 and the ds_read_b64_tr_b16 transpose read).  Best of `reps`
+    launches at each of a few grid sizes, timed with events on the launch stream."""
+    from mla_flash_attention_amd import peaks as P
+    P.lib()
+
+    def best_ms(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return min(a.elapsed_time(b) for a, b in ev)
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    out["hbm_read_gbs"] = max(nbytes / (best_ms(lambda: P.hbm_read(buf, sink, n)) * 1e-3) / 1e9
+                              for n in (2048, 4096, 8192))
+    del buf
+    fsink = torch.zeros(2048 * P.THREADS, dtype=torch.float32, device="cuda")
+    iters = 4096
+    out["mfma_bf16_tflops"] = max(
+        n * 4 * iters * 8 * P.MFMA_FLOPS / (best_ms(lambda: P.mfma_bf16(iters, 2.0 ** -10, fsink, n)) * 1e-3) / 1e12
+        for n in (512, 1024, 2048))
+    lds_iters = 8192
+    for tag, tr in (("lds_b128_gbs", False), ("lds_tr16_gbs", True)):
+        out[tag] = max(n * 4 * lds_iters * P.LDS_STEP_BYTES /
+                       (best_ms(lambda: P.lds_read(lds_iters, tr, sink, n)) * 1e-3) / 1e9 for n in (512, 1024))
+    out["lds_b128_bytes_per_cu_clk_at_2p4ghz"] = out["lds_b128_gbs"] * 1e9 / (256 * 2.4e9)
+    out["lds_tr16_bytes_per_cu_clk_at_2p4ghz"] = out["lds_tr16_gbs"] * 1e9 / (256 * 2.4e9)
+    return out
+
+
 def _cpu_baseline(p, limit_s=40.0):
     """The fp64 oracle on the host cores over the full workload (it finishes in seconds
     there); cells/s."""
@@ -335,6 +379,8 @@ def main():
     only = set(x.strip().lower() for x in args.only.split(",") if x.strip())
     want = lambda k: not only or k in only
 
+    peaks = None if args.no_peaks else _measured_peaks(torch)
+    mfma_meas = peaks["mfma_bf16_tflops"] if peaks else None
     result = {}
     if want("c2"):
         p2 = synth.make_config(2)
@@ -359,6 +405,11 @@ def main():
                          "mfma_frac": flops / (r["part_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                          "call_frac_hbm": cbytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         }
+        if peaks:
+            rf = result["roofline"]
+            rf["peak_measured"] = peaks["hbm_read_gbs"]
+            rf["frac_measured"] = achieved / peaks["hbm_read_gbs"]
+            rf["mfma_frac_measured"] = rf["mfma_tflops"] / mfma_meas
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = _cpu_baseline(p2)
     sec = {}
@@ -377,7 +428,8 @@ def main():
             tf = fl / (r["step_ms"] * 1e-3) / 1e12
             sec["c3_prefill_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
                                                       cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
-                                                      mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
+                                                      mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma",
+                                                      mfma_frac_measured=tf / mfma_meas if peaks else None)
         if want("n2"):
             # non-absorbed MLA prefill: per-head 192-wide keys, 128-wide values, the C3 chunk shape
             p = synth.make_mha_problem(2048, 128, 4096, synth.TYPE_BF16, synth.TYPE_BF16, seed=3, causal=True)
@@ -387,7 +439,8 @@ def main():
             tf = fl / (r["step_ms"] * 1e-3) / 1e12
             sec["n2_prefill_mha_2048x128h_causal"] = dict(ms=r["step_ms"], p10=r["p10"], p90=r["p90"],
                                                           cells_per_s=pairs / (r["step_ms"] * 1e-3), tflops=tf,
-                                                          mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma")
+                                                          mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS, bound="mfma",
+                                                          mfma_frac_measured=tf / mfma_meas if peaks else None)
         if want("n4"):
             # absorbed projections either side of the decode workload's attention: 4 sequences x
             # 128 heads over 32768-cell bf16 caches, plus W_UK / W_UV (16 MiB each)
@@ -434,6 +487,8 @@ def main():
                     hbm_frac_cache_once=cache_bytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
     if sec:
         result["secondary"] = sec
+    if peaks:
+        result["measured_peaks"] = peaks
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -1,4 +1,9 @@
-"""Build libmlafa.so (gfx950 only) in-tree with hipcc.
+"""Build libmlafa.so (gfx950 only) in-tree with hipcc, and libmlapeaks.so beside it.
+
+libmlafa.so is the attention library (include/mla_fa.h).  libmlapeaks.so holds the
+achievable-peak micro-benchmarks (include/mla_peaks.h) that benchmarks use to state
+roofline fractions against measured peaks; it is a library of its own so the attention
+library exports only the path.
 
 Every HIP source is compiled with packed-FP32 instructions disabled: hipcc -O3 would
 otherwise fuse scalar float code into v_pk_{add,mul,fma}_f32.
@@ -14,8 +19,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmlafa.so")
+PEAKS_LIB = os.path.join(HERE, "libmlapeaks.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["attn.hip", "mha.hip", "proj.hip", "compact.hip", "api.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -41,16 +48,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link both libraries; returns the attention library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB, verbose)
     return LIB
 
 

@@ -12,8 +12,8 @@ from mla_flash_attention_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "mla_fa.h")).read()
+def _declared(header="mla_fa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"^(?:const char \*|int |size_t )\s*(\w+)\(", text, re.M)))
 
 
@@ -29,6 +29,28 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == set(B.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_peaks_library_exports_and_validates():
+    """libmlapeaks.so (include/mla_peaks.h) loads, exports what its header declares, and
+    rejects bad arguments before launching anything."""
+    from mla_flash_attention_amd import peaks as P
+    if not os.path.exists(P.LIB_PATH):
+        pytest.fail("libmlapeaks.so is not built")
+    names = _declared("mla_peaks.h")
+    assert set(names) == set(P.EXPORTS), names
+    Lp = P.lib()
+    for n in names:
+        assert hasattr(Lp, n), n
+    sink = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation
+    assert Lp.mla_peak_hbm_read(None, 1024, sink, 1, None) == -1
+    assert Lp.mla_peak_hbm_read(ctypes.c_void_p(16), 1000, sink, 1, None) == -1     # not a multiple of 16
+    assert Lp.mla_peak_hbm_read(ctypes.c_void_p(8), 1024, sink, 1, None) == -1      # misaligned
+    assert Lp.mla_peak_hbm_read(ctypes.c_void_p(16), 1024, sink, 0, None) == -1     # no workgroups
+    assert Lp.mla_peak_mfma_bf16(0, 1.0, sink, 1, None) == -1
+    assert Lp.mla_peak_mfma_bf16(1, 1.0, None, 1, None) == -1
+    assert Lp.mla_peak_lds_read(0, 0, sink, 1, None) == -1
+    assert Lp.mla_peak_lds_read(1, 1, sink, 0, None) == -1
 
 
 def test_version_and_strerror(L):
