@@ -32,6 +32,7 @@
 //     the 512-wide O accumulators are rarely touched by the softmax.
 //   * A workgroup is NW waves = (NW/WK) head sets x WK key halves; key halves merge
 //     their (m, l, O) through LDS at the end, which halves split-KV partial traffic.
+//     Each wave of a pair merges and writes half of the 512 output columns.
 #include <type_traits>
 
 #include "mla_fa_internal.h"
@@ -79,7 +80,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     constexpr int kLdsBytes = 2 * kStageBytes + (kQ8 ? kTileBytes : 0);
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
     static_assert(kTileKeys % NW == 0 && 8 % NW == 0, "copy split over waves");
-    static_assert(WK == 1 || kHS * MB * (32 * 4 * 64 + 32) * 4 <= kLdsBytes, "key-half merge fits in LDS");
+    // key-half exchange area per head set and 16-head block: [2 waves][16 blocks][64 lanes]
+    // f32x4 of O, then m[2][16] and l[2][16]
+    constexpr int kXfer = 2 * 16 * 64 * 4 + 64;   // floats
+    static_assert(WK == 1 || kHS * MB * kXfer * 4 <= kLdsBytes, "key-half merge fits in LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kLdsBytes];
 
     const int lane = threadIdx.x & 63;
@@ -537,48 +541,54 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) l_run[mb] = wave_sum_groups(l_run[mb]);   // lane groups' sums
 
-    // ---- merge the two key halves of each head set through LDS
+    // ---- merge the two key halves of each head set through LDS.  Wave kp keeps dv column
+    // blocks 16 kp .. 16 kp + 15: it hands the partner's 16 blocks over (16-byte LDS writes),
+    // takes the partner's copy of its own 16, and both waves write half of the output.
+    // (The register array O is only ever indexed with constants: the half is a template
+    // argument of the merge step, selected by a wave-uniform branch.)
     if constexpr (WK == 2) {
         __syncthreads();                                   // tiles no longer needed
-        float *xo = reinterpret_cast<float *>(lds) + hs * MB * (32 * 4 * 64 + 32);
-        if (kp == 1) {
+        float *xs = reinterpret_cast<float *>(lds) + hs * MB * kXfer;
+        auto merge_half = [&](auto kpc) __attribute__((always_inline)) {
+            constexpr int K = decltype(kpc)::value, P = 1 - K;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                float *xb = xo + mb * (32 * 4 * 64 + 32);
+                f32x4 *xo = reinterpret_cast<f32x4 *>(xs + mb * kXfer);
+                float *xm = xs + mb * kXfer + 2 * 16 * 64 * 4;
 #pragma unroll
-                for (int nb = 0; nb < 32; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) xb[(nb * 4 + r) * 64 + lane] = o[mb][nb][r];
+                for (int j = 0; j < 16; ++j) xo[(K * 16 + j) * 64 + lane] = o[mb][16 * P + j];
                 if (lane < 16) {
-                    xb[32 * 4 * 64 + lane] = m_run[mb];
-                    xb[32 * 4 * 64 + 16 + lane] = l_run[mb];
+                    xm[K * 16 + lane] = m_run[mb];
+                    xm[32 + K * 16 + lane] = l_run[mb];
                 }
             }
-        }
-        __syncthreads();
-        if (kp == 1) return;
+            __syncthreads();
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const float *xb = xo + mb * (32 * 4 * 64 + 32);
-            const float m2 = xb[32 * 4 * 64 + l16], l2 = xb[32 * 4 * 64 + 16 + l16];
-            const float mn = fmaxf(m_run[mb], m2);
-            const float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[mb] - mn);
-            const float a2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-            l_run[mb] = a1 * l_run[mb] + a2 * l2;
-            m_run[mb] = mn;
-            float a1r[4], a2r[4];
+            for (int mb = 0; mb < MB; ++mb) {
+                const f32x4 *xo = reinterpret_cast<const f32x4 *>(xs + mb * kXfer);
+                const float *xm = xs + mb * kXfer + 2 * 16 * 64 * 4;
+                const float m2 = xm[P * 16 + l16], l2 = xm[32 + P * 16 + l16];
+                const float mn = fmaxf(m_run[mb], m2);
+                const float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[mb] - mn);
+                const float a2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+                l_run[mb] = a1 * l_run[mb] + a2 * l2;
+                m_run[mb] = mn;
+                f32x4 a1r, a2r;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                a1r[r] = shfl_f(a1, 4 * g + r);
-                a2r[r] = shfl_f(a2, 4 * g + r);
+                for (int r = 0; r < 4; ++r) {
+                    a1r[r] = shfl_f(a1, 4 * g + r);
+                    a2r[r] = shfl_f(a2, 4 * g + r);
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    o[mb][16 * K + j] = a1r * o[mb][16 * K + j] + a2r * xo[(P * 16 + j) * 64 + lane];
             }
-#pragma unroll
-            for (int nb = 0; nb < 32; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[mb][nb][r] = a1r[r] * o[mb][nb][r] + a2r[r] * xb[(nb * 4 + r) * 64 + lane];
-        }
+        };
+        if (kp == 0) merge_half(std::integral_constant<int, 0>{});
+        else merge_half(std::integral_constant<int, 1>{});
     }
+    // dv column block nb is written by this wave (with key halves: the half it merged)
+    auto owns = [&](int nb) __attribute__((always_inline)) { return WK == 1 || (nb >> 4) == kp; };
 
     // ---- write the final output (n_split == 1) or this split's partial
     if (a.n_split == 1) {
@@ -597,7 +607,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                 if (head < a.n_head) {
                     float *op = a.out + ((int64_t)row * a.n_head + head) * kDV + l16;
 #pragma unroll
-                    for (int nb = 0; nb < 32; ++nb) op[16 * nb] = o[mb][nb][r] * ir;
+                    for (int nb = 0; nb < 32; ++nb)
+                        if (owns(nb)) op[16 * nb] = o[mb][nb][r] * ir;
                 }
             }
         }
@@ -610,7 +621,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int head_l = h_base + mb * 16 + l16;
-            if (lane < 16 && head_l < a.n_head) {
+            if (kp == 0 && lane < 16 && head_l < a.n_head) {   // both key halves hold the merged m, l
                 wm[base + head_l] = m_run[mb];
                 wl[base + head_l] = l_run[mb];
             }
@@ -621,7 +632,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     if (head < a.n_head) {
                         float *op = wo + (base + head) * kDV + l16;
 #pragma unroll
-                        for (int nb = 0; nb < 32; ++nb) op[16 * nb] = o[mb][nb][r];
+                        for (int nb = 0; nb < 32; ++nb)
+                            if (owns(nb)) op[16 * nb] = o[mb][nb][r];
                     }
                 }
             }
