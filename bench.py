@@ -12,6 +12,10 @@ f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cell
 ragged 2-token decode, per-head (DK=192 / DV=128) prefill, and decode with the absorbed
 W_UK / W_UV projections either side.
 
+Every timed loop follows W warm-up calls and at least 0.1 s of warm-up load in total
+("warmup_min_seconds"): the GPU reaches its steady clock only after tens of
+milliseconds of load.
+
 Key "measured_peaks": what this GPU measurably delivers (HBM stream read, dense bf16
 MFMA issue, LDS reads; include/mla_peaks.h), so each roofline fraction is also stated
 against a measured peak ("frac_measured", "mfma_frac_measured") beside the published one.
@@ -46,7 +50,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak micro-benchmarks")
-    ap.add_argument("--only", default="", help="run only these workloads, e.g. 'c2' or 'c3,c4'")
+    ap.add_argument("--only", default="",
+                    help="run only these workloads, e.g. 'c2' or 'c3,c4' ('peaks' alone: only the measured peaks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -120,6 +125,26 @@ def _traffic(kernel_key):
     return e.get("bytes_per_launch")
 
 
+WARM_FLOOR_S = 0.1   # minimum warm-up time before every timed loop
+
+
+def _warm(fn, warmup):
+    """`warmup` untimed calls fn(0 .. warmup-1), then more until at least WARM_FLOOR_S
+    has passed: the GPU needs tens of milliseconds of load to reach its steady clock (the
+    C2 step measured ~70 us in its first ~10 ms of load and ~60 us from ~50 ms on)."""
+    import torch
+    t = time.perf_counter()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    n = warmup
+    while time.perf_counter() - t < WARM_FLOOR_S:
+        for _ in range(8):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+
+
 def _time_decode(B, p, copies, steps, warmup, n_split=0):
     """Per-call times on the launch stream.  step: the one-call API (compaction first on the
     sparse path, then attention and merge) repeated back to back between two events;
@@ -146,9 +171,7 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0):
     t1 = torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
+        _warm(fn, warmup)
         t0.record(stream)
         for i in range(steps):
             fn(i)
@@ -210,10 +233,8 @@ def _time_attend(B, p, steps, warmup, n_split=0):
         B.mla_fa_attend(q, p.q_type, kv, p.kv_type, p.scale, out, kv_len=kv_len, causal=p.causal, mask=mask,
                         alibi=alibi, sinks=sinks, softcap=p.softcap, n_split=ns, workspace=ws, stream=stream)
 
-    for _ in range(warmup):
-        call()
+    _warm(lambda i: call(), warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(steps):
         call()
@@ -229,9 +250,8 @@ def _time_prefill(B, p, steps, warmup):
     q = _dev(p.q.reshape(p.n_tok, p.n_head, synth.DK))
     kv = _dev(p.kv.reshape(p.n_kv, -1))
     out = torch.empty((p.n_tok, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        B.mla_fa_prefill(q, p.q_type, kv, p.kv_type, p.scale, out, causal=True, n_split=1, stream=stream)
-    torch.cuda.synchronize()
+    _warm(lambda i: B.mla_fa_prefill(q, p.q_type, kv, p.kv_type, p.scale, out, causal=True, n_split=1,
+                                     stream=stream), warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         evs[i][0].record(stream)
@@ -252,9 +272,7 @@ def _time_mha(B, p, steps, warmup):
     def call():
         B.mla_fa_prefill_mha(q, p.q_type, k, v, p.kv_type, p.scale, out, causal=p.causal, stream=stream)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    _warm(lambda i: call(), warmup)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         evs[i][0].record(stream)
@@ -285,10 +303,8 @@ def _time_absorbed(B, p, steps, warmup):
         B.mla_fa_absorbed(qn, qp, p.q_type, wk, wv, kv, p.kv_type, p.scale, out, causal=p.causal, n_split=ns,
                           workspace=ws, stream=stream)
 
-    for _ in range(warmup):
-        call()
+    _warm(lambda i: call(), warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(steps):
         call()
@@ -390,7 +406,8 @@ def main():
         achieved = kbytes / (r["part_ms"] * 1e-3) / 1e9
         result = {
             "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+            "warmup": args.warmup, "warmup_min_seconds": WARM_FLOOR_S,
+            "ms_per_step": r["step_ms"], "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic: seeded N(0,1) rounded to bf16, DeepSeek-V3 MLA shapes",
             "config": {"workload": "MLA decode, 4 seq x 1 token x 128 heads, latent cache n_kv=32768 x 576 bf16 "
