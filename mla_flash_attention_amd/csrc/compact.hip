@@ -13,9 +13,10 @@
 // of 8 steps issue their 8 loads back to back before any is used (a row's segments are
 // otherwise walked one memory round trip per step).  Per-lane kept
 // counts (0..8) are prefix-summed across the wave with four ballots (one per count
-// bit) and mbcnt, so the scan inside a wave costs no LDS.  The only LDS traffic is
-// the 16 segment counts.  Rows whose base is not 16-byte aligned take a one-cell-per-
-// lane path with the same structure.
+// bit) and mbcnt, so the scan inside a wave costs no LDS.  Pass 1 also leaves each
+// lane's 8 kept bits in LDS (a byte per 8 cells, for rows of up to 2^20 cells), so pass 2
+// reads the row's mask only once in all.  Rows whose base is not 16-byte aligned take a
+// one-cell-per-lane path with the same structure (and re-read the mask).
 #include "mla_fa_internal.h"
 
 namespace mlafa {
@@ -56,16 +57,23 @@ __device__ __forceinline__ void wave_scan4(unsigned c, unsigned &below, unsigned
     }
 }
 
+// Rows of up to kLdsCells cells keep pass 1's kept-bits in LDS (one byte per 8 cells, in
+// dynamic LDS sized to the row), so pass 2 reads no mask bytes from memory again.
+constexpr int64_t kLdsCells = 1 << 20;
+
 __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned short *__restrict__ mask,
                                                               int64_t row_stride, int64_t n_kv,
                                                               int32_t *__restrict__ idx,
                                                               int64_t idx_stride,
-                                                              int32_t *__restrict__ count) {
+                                                              int32_t *__restrict__ count,
+                                                              int keep_bits) {
     __shared__ unsigned seg_count[kWaves];
+    extern __shared__ unsigned char kbits[];          // byte c / 8: kept bits of cells c .. c + 7
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const unsigned short *row = mask + (int64_t)blockIdx.x * row_stride;
     int32_t *out = idx + (int64_t)blockIdx.x * idx_stride;
     const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+    const bool keep = vec && keep_bits;                // LDS bits (launch sized them for n_kv)
     const int step = vec ? 512 : 64;                         // cells per wave per load
     // contiguous segment of this wave, a whole number of load steps
     int64_t seg = (n_kv + kWaves - 1) / kWaves;
@@ -73,7 +81,8 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     const int64_t s0 = (int64_t)wave * seg;
     const int64_t s1 = s0 + seg < n_kv ? s0 + seg : n_kv;
 
-    // pass 1: count this segment's kept cells (whole batches of kBatch steps first)
+    // pass 1: count this segment's kept cells (whole batches of kBatch steps first); a
+    // lane's 8 cells start at a multiple of 8, and only bytes of this segment are written
     constexpr int kBatch = 8;
     unsigned my_total = 0;
     int64_t b = s0;
@@ -84,9 +93,13 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
             for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const u16x8 *>(row + b + 512 * u + 8 * lane);
             unsigned c = 0;
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
+            for (int u = 0; u < kBatch; ++u) {
+                unsigned k = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) c += (unsigned)(v[u][e] != kNegInf);
+                for (int e = 0; e < 8; ++e) k |= (unsigned)(v[u][e] != kNegInf) << e;
+                if (keep) kbits[(b + 512 * u) / 8 + lane] = (unsigned char)k;
+                c += __builtin_popcount(k);
+            }
             // c <= 64: the wave total by ballots over its 7 bits
 #pragma unroll
             for (int bit = 0; bit < 7; ++bit)
@@ -95,7 +108,9 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     }
     for (; b < s1; b += step) {
         if (vec) {
-            const unsigned k = kept_bits8(row, b + 8 * lane, s1);
+            const int64_t base = b + 8 * lane;
+            const unsigned k = kept_bits8(row, base, s1);
+            if (keep && base < s1) kbits[base / 8] = (unsigned char)k;
             unsigned below, tot;
             wave_scan4(__builtin_popcount(k), below, tot);
             my_total += tot;
@@ -116,19 +131,30 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     }
     if (threadIdx.x == 0) count[blockIdx.x] = (int32_t)all;
 
-    // pass 2: write this segment's kept cells, ascending (whole batches first)
+    // pass 2: write this segment's kept cells, ascending (whole batches first); the kept
+    // bits come from LDS when pass 1 left them there, else from the mask again
     b = s0;
     if (vec) {
         for (; b + kBatch * 512 <= s1; b += kBatch * 512) {
-            u16x8 v[kBatch];
+            unsigned kk[kBatch];
+            if (keep) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const u16x8 *>(row + b + 512 * u + 8 * lane);
+                for (int u = 0; u < kBatch; ++u) kk[u] = kbits[(b + 512 * u) / 8 + lane];
+            } else {
+                u16x8 v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) v[u] = *reinterpret_cast<const u16x8 *>(row + b + 512 * u + 8 * lane);
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    kk[u] = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kk[u] |= (unsigned)(v[u][e] != kNegInf) << e;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int64_t base = b + 512 * u + 8 * lane;
-                unsigned k = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) k |= (unsigned)(v[u][e] != kNegInf) << e;
+                unsigned k = kk[u];
                 unsigned below, tot;
                 wave_scan4(__builtin_popcount(k), below, tot);
                 unsigned pos = offset + below;
@@ -144,7 +170,7 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     for (; b < s1; b += step) {
         if (vec) {
             const int64_t base = b + 8 * lane;
-            unsigned k = kept_bits8(row, base, s1);
+            unsigned k = keep ? (base < s1 ? (unsigned)kbits[base / 8] : 0u) : kept_bits8(row, base, s1);
             unsigned below, tot;
             wave_scan4(__builtin_popcount(k), below, tot);
             unsigned pos = offset + below;
@@ -169,9 +195,13 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,
                           hipStream_t stream) {
-    hipLaunchKernelGGL(compact_kernel, dim3(n_rows), dim3(kWaves * 64), 0, stream,
+    // kept-bits in LDS for rows of up to kLdsCells cells: ceil(n_kv / 8) bytes, rounded to
+    // whole 64-byte steps of a wave's segment
+    const int keep = n_kv <= kLdsCells ? 1 : 0;
+    const size_t bytes = keep ? (size_t)((n_kv + 511) / 512 * 64) : 0;
+    hipLaunchKernelGGL(compact_kernel, dim3(n_rows), dim3(kWaves * 64), bytes, stream,
                        reinterpret_cast<const unsigned short *>(mask), mask_row_stride, n_kv, idx,
-                       idx_row_stride, count);
+                       idx_row_stride, count, keep);
     return hipGetLastError();
 }
 

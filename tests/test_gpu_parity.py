@@ -240,3 +240,27 @@ def test_compaction_cases(case, aligned):
     for r in range(3):
         assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
         assert np.all(ii[r, ci[r]:] == -9)        # untouched past the count
+
+
+@pytest.mark.parametrize("n", [(1 << 20) - 5, 1 << 20, (1 << 20) + 517])
+def test_compaction_long_rows(n):
+    """Rows of up to 2^20 cells keep their kept bits in LDS between the two passes; longer
+    rows read the mask twice.  Both sides of that limit, bit-exact."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    g = np.random.default_rng(n)
+    m = np.stack([synth.sparse_runs_mask(n, g, max_gap=2312, max_run=256) for _ in range(2)])
+    stride = n + 8 - n % 8
+    host = np.full(2 * stride, 0x1234, np.uint16)
+    host.reshape(2, stride)[:, :n] = m
+    mask = to_dev(host).view(2, stride)[:, :n]
+    idx = torch.full((2, n), -9, dtype=torch.int32, device="cuda")
+    cnt = torch.full((2,), -9, dtype=torch.int32, device="cuda")
+    B.fa_mask_compact(mask, idx, cnt)
+    torch.cuda.synchronize()
+    idx_ref, cnt_ref = oracle.mask_compact(m)
+    ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(ci, cnt_ref)
+    for r in range(2):
+        assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
+        assert np.all(ii[r, ci[r]:] == -9)
