@@ -104,8 +104,9 @@ def _dev(a):
 
 
 def _source_hash():
+    """Hash of the sources that decide the split-attention kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
+    for f in ("attn.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
         with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
