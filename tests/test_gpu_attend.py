@@ -104,3 +104,13 @@ def test_pair_shape_request_falls_back_with_extras(monkeypatch):
 def test_small_head_counts(n_head):
     _case(f"h{n_head} extras", 0, n_seq=2, n_tok=2, n_head=n_head, n_kv=400, seed=49 + n_head, ragged=True,
           causal=True, sinks=True, alibi=True, mask_kind="distance")
+
+
+@pytest.mark.parametrize("variant", ["plain", "softcap_sinks_alibi"])
+def test_ragged_full_size(variant):
+    """The benched ragged workload at full size in its launch configuration: 8 sequences of
+    U{2..32768} valid cells x 2 causal query tokens x 128 heads, automatic split count;
+    plain, and with softcap 50, sinks and ALiBi over a distance mask.  Whole output."""
+    kw = {} if variant == "plain" else dict(softcap=50.0, sinks=True, alibi=True, mask_kind="distance")
+    _case(f"ragged full {variant}", 0, n_seq=8, n_tok=2, n_head=128, n_kv=32768, seed=6, ragged=True,
+          causal=True, **kw)
