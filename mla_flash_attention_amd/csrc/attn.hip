@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     }
     if (split >= a.n_split) return;
     const int n_rows = a.n_seq * a.n_tok;
-    const int row_lin = (int)blockIdx.y;
+    const int row_lin = (int)blockIdx.y + a.row_base;
     const int s_idx = row_lin / a.n_tok;
     const int t_idx = a.n_tok - 1 - row_lin % a.n_tok;   // longest causal rows first
     const int row = s_idx * a.n_tok + t_idx;
@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
     }
     if (split >= a.n_split) return;
     const int n_rows = a.n_seq * a.n_tok;
-    const int row_lin = (int)blockIdx.y;
+    const int row_lin = (int)blockIdx.y + a.row_base;
     const int s_idx = row_lin / a.n_tok;
     const int t_idx = a.n_tok - 1 - row_lin % a.n_tok;
     const int row = s_idx * a.n_tok + t_idx;
@@ -1176,11 +1176,25 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     }
 }
 
+// One launch per kMaxGridY query rows (the grid's y extent); a.row_base tells each launch
+// where its rows start.
+template <typename K>
+hipError_t launch_rows(K kernel, const AttnArgs &a, int threads, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.n_seq * a.n_tok;
+    for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridY) {
+        AttnArgs b = a;
+        b.row_base = (int)r0;
+        const int n = (int)(rows - r0 < kMaxGridY ? rows - r0 : kMaxGridY);
+        hipLaunchKernelGGL(kernel, dim3(a.grid_x, n), dim3(threads), 0, stream, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int MB, int NW, int WK, int KIND, bool IDX>
 hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
-    dim3 grid(a.grid_x, a.n_seq * a.n_tok);
-    hipLaunchKernelGGL((attn_kernel<MB, NW, WK, KIND, IDX>), grid, dim3(NW * 64), 0, stream, a);
-    return hipGetLastError();
+    return launch_rows(attn_kernel<MB, NW, WK, KIND, IDX>, a, NW * 64, stream);
 }
 
 // Per-sequence lengths, ALiBi, sinks and softcap run in the single-wave kernel only.
@@ -1188,9 +1202,7 @@ bool uses_extras(const AttnArgs &a) { return a.kv_len || a.alibi || a.sinks || a
 
 template <int NP, int KIND, bool IDX>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t stream) {
-    dim3 grid(a.grid_x, a.n_seq * a.n_tok);
-    hipLaunchKernelGGL((attn_pair_kernel<NP, KIND, IDX>), grid, dim3(NP * 128), 0, stream, a);
-    return hipGetLastError();
+    return launch_rows(attn_pair_kernel<NP, KIND, IDX>, a, NP * 128, stream);
 }
 
 template <int KIND, bool IDX>

@@ -47,7 +47,10 @@ struct AttnArgs {
     const float *sinks;            // [n_head] sink logits (natural log), or nullptr
     float cap_in;                  // softcap: score = cap_out * tanh(dot * cap_in) in log2 units;
     float cap_out;                 //   cap_in = 0 means no softcap
+    int row_base;                  // query row of blockIdx.y = 0 (launches cover at most
+                                   //   kMaxGridY rows each)
 };
+constexpr int kMaxGridY = 65535;   // rows per launch (the grid's y extent)
 
 // Partial layout inside the workspace, for R = n_seq*n_tok rows, H heads, S splits:
 //   m [S][R][H] fp32 (log2 domain), l [S][R][H] fp32, o [S][R][H][512] fp32.

@@ -264,3 +264,30 @@ def test_compaction_long_rows(n):
     for r in range(2):
         assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
         assert np.all(ii[r, ci[r]:] == -9)
+
+
+# ---------------------------------------------------------------- rows past one launch
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_rows_past_the_grid_limit(kind):
+    """More query rows than one launch's grid holds (65535): 70,000 rows whose inputs repeat
+    every 1000 rows.  Every row must equal its twin among the first 1000 bitwise, and
+    those match the oracle."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    reps = 70
+    if kind == "decode":
+        p = synth.make_problem(kind="decode", n_seq=1000, n_head=16, n_kv=40, seed=77)
+        q = to_dev(p.q.reshape(p.n_seq, p.n_head, synth.DK)).repeat(reps, 1, 1)
+        kv = to_dev(p.kv).repeat(reps, 1, 1)
+        out = torch.empty((reps * p.n_seq, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+        B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, n_split=1)
+    else:
+        p = synth.make_problem(kind="prefill", n_tok=1000, n_head=16, n_kv=40, seed=78, causal=False)
+        q = to_dev(p.q.reshape(p.n_tok, p.n_head, synth.DK)).repeat(reps, 1, 1)
+        kv = to_dev(p.kv.reshape(p.n_kv, -1))
+        out = torch.empty((reps * p.n_tok, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+        B.mla_fa_prefill(q, p.q_type, kv, p.kv_type, p.scale, out, causal=False, n_split=1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(reps, -1, p.n_head, synth.DV)
+    assert np.array_equal(got, np.broadcast_to(got[:1], got.shape)), "rows past 65535 differ from their twins"
+    assert_parity(got[0].reshape(-1, synth.DV).astype(np.float64), oracle.attention_problem(p), f"{kind} first rows")
