@@ -36,7 +36,9 @@
  *     bf16/Q8_0.  A Q8_0 row is 18 blocks of {f16 scale d, 32 int8 codes} = 612
  *     bytes; value = code * d.  Q8_0 is computed in f16 on the GPU, f16 caches in
  *     f16 and bf16 caches in bf16, all with fp32 accumulation.
- *   - n_head is a multiple of 16 in [16, 128].
+ *   - n_head is a multiple of 16 in [16, 128].  Query rows (n_seq * n_tok) times
+ *     n_head is at most 2^31 - 1; more is MLA_FA_ERR_INVALID.  Any number of rows
+ *     within that runs: calls beyond 65535 rows are issued as several launches.
  *   - Outputs are fp32 [..][n_head][512].
  */
 #ifndef MLA_FA_H

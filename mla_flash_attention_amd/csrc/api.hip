@@ -134,7 +134,7 @@ int validate(const Common &c) {
     st = check_heads(c.n_head);
     if (st) return st;
     if (c.n_seq < 1 || c.n_tok < 1 || c.n_kv < 1 || c.n_kv > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
-    if ((int64_t)c.n_seq * c.n_tok > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;
+    if ((int64_t)c.n_seq * c.n_tok * c.n_head > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;   // merge grid
     if (!std::isfinite(c.scale)) return MLA_FA_ERR_INVALID;
     if (c.n_split < 0 || c.n_split > kMaxSplits) return MLA_FA_ERR_INVALID;
     if (!aligned(c.q, 16) || !aligned(c.out, 16)) return MLA_FA_ERR_INVALID;
@@ -208,6 +208,7 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
 int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *ws, size_t ws_bytes,
               hipStream_t stream, const float *sinks = nullptr) {
     if (n_split <= 1) return MLA_FA_OK;
+    if (n_rows * n_head > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;   // one merge workgroup per (row, head)
     const size_t need = partial_bytes(n_rows, n_head, n_split);
     if (!ws || ws_bytes < need || !aligned(ws, 16)) return MLA_FA_ERR_WORKSPACE;
     hipError_t e = launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws), out, sinks,

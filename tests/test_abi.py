@@ -110,6 +110,7 @@ def _decode(L, **kw):
     (dict(n_seq=2, mask=FAKE, ms=10), B.MLA_FA_ERR_INVALID),    # mask rows overlap
     (dict(kvt=B.MLA_FA_Q8_0, rs=600), B.MLA_FA_ERR_INVALID),    # Q8_0 row is 612 bytes
     (dict(kvt=B.MLA_FA_Q8_0, rs=614), B.MLA_FA_ERR_INVALID),    # Q8_0 stride not 4-aligned
+    (dict(n_seq=1 << 24), B.MLA_FA_ERR_INVALID),                # rows x heads past the merge grid
 ])
 def test_decode_validation(L, kw, status):
     assert _decode(L, **kw) == status
@@ -122,6 +123,12 @@ def test_prefill_validation(L):
     assert f(n_tok=17, n_kv=16) == B.MLA_FA_ERR_INVALID            # causal chunk longer than cache
     assert f(q=None) == B.MLA_FA_ERR_INVALID
     assert f(n_tok=0) == B.MLA_FA_ERR_INVALID
+
+
+def test_merge_grid_limit(L):
+    """One merge workgroup per (row, head): rows x heads beyond 2^31 - 1 is rejected before
+    any launch."""
+    assert L.mla_fa_merge_partials(1 << 24, 128, 4, FAKE, FAKE, 1 << 62, None) == B.MLA_FA_ERR_INVALID
 
 
 def test_compact_validation(L):
