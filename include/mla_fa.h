@@ -97,7 +97,9 @@ size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, 
  *   idx_seq_stride is an ascending list of cache rows to attend to (as written by
  *                  fa_mask_compact); both arrays live on the device, the count is
  *                  read by the kernels, so there is no host synchronisation.  The
- *                  mask, if given, is still added at the gathered rows.
+ *                  mask, if given, is still added at the gathered rows.  Entries
+ *                  must lie in [0, n_kv); the kernels clamp any that do not (the
+ *                  result is then unspecified, but no read leaves the cache).
  *   scale          finite fp32 softmax scale (e.g. 1/sqrt(192)).
  *   out            [n_seq][n_head][512] fp32.
  *   n_split        0 = automatic, else 1 .. 1024 KV splits.

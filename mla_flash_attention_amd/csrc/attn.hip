@@ -57,6 +57,13 @@ __device__ __forceinline__ int rope_slot(int r, int c) { return 128 * r + 16 * (
 constexpr int kQ8TileBytes = kTileKeys * kQ8RowBytes;     // 39,168
 constexpr float kRescaleThresh = 8.0f;                    // log2 units
 
+// An index-list entry clamped into [0, n_kv): a list with entries out of range gives an
+// unspecified result but never a read outside the cache.
+__device__ __forceinline__ int clamp_row(int v, int64_t n_kv) {
+    const int hi = (int)(n_kv - 1);
+    return v < 0 ? 0 : (v > hi ? hi : v);
+}
+
 // ---------------------------------------------------------------------------------
 // The attention kernel.  NW waves, each owning MB blocks of 16 heads; WK waves share
 // one head set and split every 64-key tile between them (WK = 2: keys 0..31 /
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     if constexpr (IDX) {
         int64_t pos = k0 + lane;
         if (pos >= k1) pos = k1 - 1;
-        if (n_tiles > 0) idx0 = irow[pos];
+        if (n_tiles > 0) idx0 = clamp_row(irow[pos], a.n_kv);
     }
 
     // Copy tile `it` into stage `dst` (HBM -> LDS; raw bytes for Q8_0) together with its
@@ -242,7 +249,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         asm volatile("" : "+v"(ln));
         int my_idx = 0;                                    // cache row of list position kt + lane
         if constexpr (IDX)
-            my_idx = it == 0 ? idx0 : reinterpret_cast<const int *>(idx_src + kIdxOff)[ln];
+            my_idx = it == 0 ? idx0 : clamp_row(reinterpret_cast<const int *>(idx_src + kIdxOff)[ln], a.n_kv);
         if (mrow) {
             const int r = ln < last ? ln : last;
             const int64_t col = IDX ? (int64_t)shfl_int(my_idx, r) : kt + r;
@@ -757,7 +764,7 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
     if constexpr (IDX) {
         int64_t pos = k0 + lane;
         if (pos >= k1) pos = k1 - 1;
-        if (n_st > 0) idx0 = irow[pos];
+        if (n_st > 0) idx0 = clamp_row(irow[pos], a.n_kv);
     }
 
     // Copy stage n into `dst`: 32 latent rows (one full-wave copy each), the RoPE bytes of
@@ -783,7 +790,7 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
         if constexpr (IDX) {
             int ln = lane;
             asm volatile("" : "+v"(ln));
-            c.my_idx = n == 0 ? idx0 : reinterpret_cast<const int *>(idx_src + kPIdxOff)[ln];
+            c.my_idx = n == 0 ? idx0 : clamp_row(reinterpret_cast<const int *>(idx_src + kPIdxOff)[ln], a.n_kv);
         }
         c.tbase = IDX ? kvs : kvs + c.kt * a.kv_row_stride;
         return c;

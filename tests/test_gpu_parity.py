@@ -291,3 +291,33 @@ def test_rows_past_the_grid_limit(kind):
     got = out.cpu().numpy().reshape(reps, -1, p.n_head, synth.DV)
     assert np.array_equal(got, np.broadcast_to(got[:1], got.shape)), "rows past 65535 differ from their twins"
     assert_parity(got[0].reshape(-1, synth.DV).astype(np.float64), oracle.attention_problem(p), f"{kind} first rows")
+
+
+def test_sparse_index_out_of_range_is_clamped():
+    """Index-list entries outside [0, n_kv) are clamped in the kernel (documented: the
+    result is then unspecified, but every read stays inside the cache).  A list with such
+    entries gives exactly the output of the same list clamped on the host."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="decode", n_seq=2, n_head=16, n_kv=3000, seed=79)
+    g = np.random.default_rng(79)
+    good = np.stack([np.sort(g.choice(p.n_kv, 900, replace=False)) for _ in range(2)]).astype(np.int64)
+    bad = good.copy()
+    bad[0, [0, 100, 899]] = [-3, p.n_kv + 5, 1 << 30]
+    bad[1, [1, 64, 65]] = [-(1 << 30), p.n_kv, -1]
+    outs = []
+    for lst in (bad, np.clip(bad, 0, p.n_kv - 1)):
+        q = to_dev(p.q.reshape(p.n_seq, p.n_head, synth.DK))
+        kv = to_dev(p.kv)
+        full = np.zeros((2, p.n_kv), np.int32)          # index rows are n_kv apart
+        full[:, :900] = lst
+        idx = torch.from_numpy(full).cuda()
+        cnt = torch.full((2,), 900, dtype=torch.int32, device="cuda")
+        out = torch.empty((p.n_seq, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+        ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, 3)
+        B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, kv_idx=idx, kv_idx_count=cnt, n_split=3,
+                        workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(outs[0], outs[1])
