@@ -44,7 +44,7 @@ METRIC = "MLA FA latent KV cells/s per GPU + % of HBM / MFMA roofline"
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotating input copies (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
