@@ -88,7 +88,8 @@ size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, 
  *   q              [n_seq][n_head][576] f16/bf16 bits (16-byte aligned).
  *   kv             row j of sequence s at kv + s*kv_seq_stride + j*kv_row_stride
  *                  (bytes).  f16/bf16: 16-byte aligned base and strides; Q8_0:
- *                  4-byte aligned.  kv_seq_stride may be 0 (shared cache).
+ *                  4-byte aligned, kv_row_stride at most 2^26.  kv_seq_stride may
+ *                  be 0 (shared cache).
  *   n_kv           rows per sequence, 1 .. 2^31-1.
  *   mask           NULL, or f16 bits [n_seq][mask_seq_stride] (elements); element
  *                  (s, j) is added to score j of every head of sequence s.

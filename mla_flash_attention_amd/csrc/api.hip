@@ -142,6 +142,8 @@ int validate(const Common &c) {
     if (!aligned(c.kv, kva) || c.kv_row_stride < row_bytes(c.kv_type) || c.kv_row_stride % kva ||
         c.kv_seq_stride < 0 || c.kv_seq_stride % kva)
         return MLA_FA_ERR_INVALID;
+    // Q8_0 tiles address their rows with 32-bit offsets from the tile's first row
+    if (c.kv_type == MLA_FA_Q8_0 && c.kv_row_stride > (int64_t)1 << 26) return MLA_FA_ERR_INVALID;
     if (c.causal && !c.kv_len && c.n_tok > c.n_kv) return MLA_FA_ERR_INVALID;
     if (c.mask) {
         if (!aligned(c.mask, 2) || c.mask_seq_stride < 0 || c.mask_tok_stride < 0)

@@ -305,6 +305,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     if constexpr (IDX)
                         src = tbase + (int64_t)shfl_int(my_idx, r) * a.kv_row_stride + c * 4;
                     else
+                        // 32-bit offset within the tile: the host bounds the row stride
+                        // by 2^26 bytes, so 63 rows + one row never wrap
                         src = tbase + (uint32_t)(r * (uint32_t)a.kv_row_stride + c * 4);
                     __builtin_amdgcn_global_load_lds((const void *)src, (LDS_PTR(void))(dst + blk * 256), 4, 0, 0);
                 }

@@ -110,6 +110,7 @@ def _decode(L, **kw):
     (dict(n_seq=2, mask=FAKE, ms=10), B.MLA_FA_ERR_INVALID),    # mask rows overlap
     (dict(kvt=B.MLA_FA_Q8_0, rs=600), B.MLA_FA_ERR_INVALID),    # Q8_0 row is 612 bytes
     (dict(kvt=B.MLA_FA_Q8_0, rs=614), B.MLA_FA_ERR_INVALID),    # Q8_0 stride not 4-aligned
+    (dict(kvt=B.MLA_FA_Q8_0, rs=(1 << 26) + 4), B.MLA_FA_ERR_INVALID),  # Q8_0 stride past 2^26 B
     (dict(n_seq=1 << 24), B.MLA_FA_ERR_INVALID),                # rows x heads past the merge grid
 ])
 def test_decode_validation(L, kw, status):

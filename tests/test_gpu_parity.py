@@ -321,3 +321,12 @@ def test_sparse_index_out_of_range_is_clamped():
         outs.append(out.cpu().numpy())
     assert np.all(np.isfinite(outs[0]))
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_cache_past_2gib():
+    """One sequence over a 2,000,003-row bf16 cache (2.3 GB: row offsets past 2^31 bytes),
+    automatic split count; the whole output against the oracle."""
+    p = synth.make_problem(kind="decode", n_seq=1, n_head=16, n_kv=2_000_003, seed=80)
+    assert p.n_kv * 1152 > (1 << 31)
+    got, _ = run_decode(p)
+    assert_parity(got, oracle.attention_problem(p), "decode 2.3 GB cache")
