@@ -293,6 +293,18 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             // raw Q8_0 rows of 612 bytes, packed back to back (153 dwords each)
             constexpr int kDw = kQ8TileBytes / 4;              // 9792 = 153 * 64
             constexpr int kBlocks = kDw / 64;                  // 153 wave-wide 256 B copies
+            // A full tile of a packed cache (row stride 612) is one contiguous block in
+            // memory too: copy it without splitting dwords into (row, column).
+            const bool contiguous = !IDX && a.kv_row_stride == kQ8RowBytes && last == kTileKeys - 1;
+            if (contiguous) {
+#pragma unroll
+                for (int j = 0; j < (kBlocks + NW - 1) / NW; ++j) {
+                    const int blk = wave + j * NW;
+                    if (blk < kBlocks)
+                        __builtin_amdgcn_global_load_lds((const void *)(tbase + (uint32_t)(blk * 256 + ln * 4)),
+                                                         (LDS_PTR(void))(dst + blk * 256), 4, 0, 0);
+                }
+            } else
 #pragma unroll
             for (int j = 0; j < (kBlocks + NW - 1) / NW; ++j) {
                 const int blk = wave + j * NW;

@@ -330,3 +330,24 @@ def test_decode_cache_past_2gib():
     assert p.n_kv * 1152 > (1 << 31)
     got, _ = run_decode(p)
     assert_parity(got, oracle.attention_problem(p), "decode 2.3 GB cache")
+
+
+@pytest.mark.parametrize("kv_type", [Q8, BF16])
+def test_decode_padded_cache_rows(kv_type):
+    """Cache rows stored at a padded stride (Q8_0: 640 B for 612, bf16: 1280 B for 1152),
+    so no tile is one contiguous block; sizes with full and ragged tiles."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="decode", n_seq=2, n_head=128, n_kv=3000, kv_type=kv_type, seed=81)
+    row = p.kv.shape[-1]
+    pad = 640 if kv_type == Q8 else 1280 // 2        # bytes for Q8_0 rows; elements for 16-bit
+    padded = np.zeros(p.kv.shape[:-1] + (pad,), dtype=p.kv.dtype)
+    padded[..., :row] = p.kv
+    kv = to_dev(padded)[..., :row]                   # strided view: row stride = the padded row
+    q = to_dev(p.q.reshape(p.n_seq, p.n_head, synth.DK))
+    out = torch.empty((p.n_seq, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, 0)
+    B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, workspace=ws)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy().reshape(-1, synth.DV).astype(np.float64), oracle.attention_problem(p),
+                  f"padded rows {kv_type}")
