@@ -263,6 +263,26 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             // 8q + l/8, slot l%8 holding chunk (l%8) ^ swizzle).  Rows past the range
             // re-read the last valid row.
             const int voff = ln * 16;
+            // A full tile of a packed cache (row stride 1152) needs no clamping and only
+            // 32-bit offsets; other tiles clamp rows past the range and scale by the stride.
+            const bool contiguous = !IDX && a.kv_row_stride == kRowBytes16 && last == kTileKeys - 1;
+            if (contiguous) {
+#pragma unroll
+                for (int j = 0; j < kTileKeys / NW; ++j) {
+                    const int r = wave + j * NW;
+                    __builtin_amdgcn_global_load_lds((const void *)(tbase + (uint32_t)(r * kRowBytes16 + voff)),
+                                                     (LDS_PTR(void))(dst + r * kVRow), 16, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 8 / NW; ++j) {
+                    const int q = wave + j * NW;
+                    const int r = 8 * q + (ln >> 3);
+                    const int chunk = (ln & 7) ^ ((r >> 1) & 7);
+                    __builtin_amdgcn_global_load_lds(
+                        (const void *)(tbase + (uint32_t)(r * kRowBytes16 + 1024 + 16 * chunk)),
+                        (LDS_PTR(void))(dst + kRopeOff + q * 1024), 16, 0, 0);
+                }
+            } else {
 #pragma unroll
             for (int j = 0; j < kTileKeys / NW; ++j) {
                 const int r = wave + j * NW;                   // tile row (wave-uniform)
@@ -288,6 +308,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     src = tbase + (int64_t)rc * a.kv_row_stride;
                 __builtin_amdgcn_global_load_lds((const void *)(src + 1024 + 16 * chunk),
                                                  (LDS_PTR(void))(dst + kRopeOff + q * 1024), 16, 0, 0);
+            }
             }
         } else {
             // raw Q8_0 rows of 612 bytes, packed back to back (153 dwords each)
