@@ -387,7 +387,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is design-only in this build)", file=sys.stderr)
+              "(sharding across GPUs is a design only; this benchmark runs on one GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     from mla_flash_attention_amd import binding as B

@@ -56,7 +56,7 @@ enum mla_fa_type { MLA_FA_F16 = 1, MLA_FA_BF16 = 2, MLA_FA_Q8_0 = 3 };
 enum mla_fa_status {
     MLA_FA_OK = 0,
     MLA_FA_ERR_INVALID = -1,      /* null pointer, bad size, stride or alignment     */
-    MLA_FA_ERR_UNSUPPORTED = -2,  /* type pair or head count this build does not do   */
+    MLA_FA_ERR_UNSUPPORTED = -2,  /* type pair or head count the library does not do */
     MLA_FA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required       */
     MLA_FA_ERR_HIP = -4           /* a HIP launch failed                              */
 };

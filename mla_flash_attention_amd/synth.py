@@ -16,7 +16,7 @@ Storage formats (what the pages fix):
   * the flash-attention mask is f16, with -inf marking cells that are not kept
     ("baguaai Flash Attention tag page", digest on the f16 FA mask PR).
 
-Recipe (stated in the design doc as well): numpy Generator(PCG64(seed*1000 + stream)),
+Recipe: numpy Generator(PCG64(seed*1000 + stream)),
 stream 0 = Q, 1 = cache, 2 = mask; values standard_normal(float32), rounded to
 nearest-even into f16/bf16, or quantised to Q8_0 with d = amax/127.
 """
