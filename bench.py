@@ -8,7 +8,7 @@ every input already resident in HBM.  Timed steps rotate over 4 copies of the in
 HBM.  Prints one JSON line (see the repository's bench contract).
 
 Secondary lines (same JSON object, key "secondary"): the other workloads - 16-head
-f16 decode, 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells,
+f16 decode (warm, and cold: caches flushed before each call), 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells (warm and cold),
 ragged 2-token decode, per-head (DK=192 / DV=128) prefill, and decode with the absorbed
 W_UK / W_UV projections either side.
 
@@ -215,6 +215,44 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0):
     return dict(total_ms=step_ms * steps, step_ms=step_ms, part_ms=part_ms,
                 part_ms_p10=float(np.percentile(single_ms, 10)), part_ms_p90=float(np.percentile(single_ms, 90)),
                 merge_ms=merge_ms, compact_ms=compact_ms, n_split=ns, kept=kept)
+
+
+def _time_decode_cold(B, p, calls=30):
+    """One-call decode (compaction first on the sparse path) with the caches cold: before
+    every call an untimed 512 MB write evicts the 256 MB last-level cache; each call is
+    timed alone between events on the launch stream.  Returns the median, p10 and p90."""
+    import torch
+    from mla_flash_attention_amd import synth
+    stream = torch.cuda.current_stream()
+    q = _dev(p.q.reshape(p.n_seq, p.n_head, synth.DK))
+    kv = _dev(p.kv)
+    mask = None if p.mask is None else _dev(p.mask.reshape(p.n_seq, p.n_kv))
+    out = torch.empty((p.n_seq, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    ns = B.mla_fa_auto_splits(p.n_seq, p.n_head, p.n_kv, p.kv_type)
+    ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, ns)
+    sparse = p.kind == "sparse"
+    idx = torch.empty((p.n_seq, p.n_kv), dtype=torch.int32, device="cuda") if sparse else None
+    cnt = torch.empty((p.n_seq,), dtype=torch.int32, device="cuda") if sparse else None
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")     # 512 MB
+
+    def call():
+        if sparse:
+            B.fa_mask_compact(mask, idx, cnt, stream=stream)
+        B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, mask=mask, kv_idx=idx, kv_idx_count=cnt,
+                        n_split=ns, workspace=ws, stream=stream)
+
+    _warm(lambda i: call(), 3)
+    evs = []
+    for i in range(calls):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return dict(ms=float(np.median(ms)), p10=float(np.percentile(ms, 10)), p90=float(np.percentile(ms, 90)))
 
 
 def _time_attend(B, p, steps, warmup, n_split=0):
@@ -438,6 +476,9 @@ def main():
             cells, kb, cb, fl = _algo_decode(p)
             sec["c1_decode_16h_f16_warm"] = dict(ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3),
                                                  kernel_ms=r["part_ms"], n_split=r["n_split"])
+            rc = _time_decode_cold(B, p)
+            sec["c1_decode_16h_f16_cold"] = dict(ms=rc["ms"], p10=rc["p10"], p90=rc["p90"],
+                                                 cells_per_s=cells / (rc["ms"] * 1e-3))
         if want("c3"):
             p = synth.make_config(3)
             r = _time_prefill(B, p, max(5, args.steps // 5), max(2, args.warmup // 5))
@@ -487,6 +528,9 @@ def main():
                                                  kept=r["kept"], n_split=r["n_split"],
                                                  scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
                                                  kept_cells_per_s=r["kept"] / (r["step_ms"] * 1e-3))
+            rc = _time_decode_cold(B, p)
+            sec["c5_sparse_131072_cells_cold"] = dict(ms=rc["ms"], p10=rc["p10"], p90=rc["p90"],
+                                                      scanned_cells_per_s=p.n_kv / (rc["ms"] * 1e-3))
         if want("n3"):
             # ragged multi-token decode: 8 sequences of U{2..32768} valid cells, 2 query tokens
             # each (causal), 128 heads; plain, then with softcap 50, sinks and ALiBi over a
