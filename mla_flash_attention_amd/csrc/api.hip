@@ -13,7 +13,7 @@ using namespace mlafa;
 namespace {
 
 constexpr int kCUs = 256;                    // MI355X compute units (one workgroup each)
-constexpr int kMinTilesPerSplit = 2;
+constexpr int kMinTilesPerSplit = 1;   // short caches: one tile per split is fastest (latency-bound)
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
