@@ -40,6 +40,11 @@
  *     n_head is at most 2^31 - 1; more is MLA_FA_ERR_INVALID.  Any number of rows
  *     within that runs: calls beyond 65535 rows are issued as several launches.
  *   - Outputs are fp32 [..][n_head][512].
+ *   - Tuning overrides, read from the environment at each call (results change by
+ *     floating-point reassociation only): MLA_FA_NSPLIT=<1..1024> forces the split
+ *     count of automatic plans; MLA_FA_SHAPE=16|32|64|128|p64|p128 forces the
+ *     heads-per-workgroup shape; MLA_FA_LOG (any value) prints each call's plan to
+ *     stderr.
  */
 #ifndef MLA_FA_H
 #define MLA_FA_H
