@@ -110,3 +110,33 @@ def test_random_compaction(case):
     for r in range(n_rows):
         assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]]), what
         assert np.all(ii[r, ci[r]:] == -9), what
+
+
+@pytest.mark.parametrize("case", range(N_CASES // 2))
+def test_random_prefill_mha(case):
+    from tests.test_gpu_mha import ref_mha, run_mha
+    g = np.random.default_rng(9400 + case)
+    t = [BF16, F16][int(g.integers(2))]
+    n_kv = int(g.integers(1, 1500))
+    causal = bool(g.random() < 0.7)
+    n_tok = int(g.integers(1, n_kv + 1)) if causal else int(g.integers(1, 600))
+    kw = dict(n_tok=n_tok, n_head=int(g.integers(1, 5)), n_kv=n_kv, q_type=t, kv_type=t,
+              seed=int(g.integers(1 << 30)), causal=causal)
+    if g.random() < 0.3:
+        kw["mask_kind"] = "runs_bias"
+    p = synth.make_mha_problem(**kw)
+    assert_parity(run_mha(p), ref_mha(p), f"per-head prefill case {case}: {kw}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES // 3))
+def test_random_absorbed(case):
+    from tests.test_gpu_absorbed import ref_absorbed, run_absorbed
+    g = np.random.default_rng(9500 + case)
+    q_type, kv_type = _types(g)
+    n_tok = int(g.integers(1, 4))
+    kw = dict(n_seq=int(g.integers(1, 4)), n_tok=n_tok, n_head=16 * int(g.integers(1, 5)),
+              n_kv=int(g.integers(n_tok, 2000)), q_type=q_type, kv_type=kv_type, seed=int(g.integers(1 << 30)),
+              causal=bool(g.random() < 0.5), ragged=bool(g.random() < 0.5))
+    p = synth.make_absorbed_problem(**kw)
+    n_split = int(g.choice([0, 1, 3]))
+    assert_parity(run_absorbed(p, n_split=n_split), ref_absorbed(p), f"absorbed case {case}: {kw} n_split={n_split}")
