@@ -352,6 +352,65 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         }
     };
 
+    // The same copies of a 16-bit tile, issued one at a time: with eight waves the copies
+    // of tile it+1 are spread over the Q.K^T steps of tile it instead of issued as one
+    // burst at the top of the step.  LDS-DMA copies pass the memory pipeline at ~30
+    // cycles per KiB, so a burst of a whole tile (72 copies per CU) held the second wave
+    // of every SIMD at its copy issue for ~2k cycles while its MFMAs waited.  Copy j of a
+    // wave: latent row wave + NW j (j < kTileKeys / NW), else the RoPE slots of rows
+    // 8q .. 8q + 7, q = wave + NW (j - kTileKeys / NW).  Row addresses are clamped as in
+    // issue_tile (a no-op for full tiles) and computed in scalar registers.
+    constexpr int kCopies = (kTileKeys + 8) / NW;          // copies per wave and tile
+    struct TileSrc {
+        const uint8_t *base;
+        int64_t kt;
+        int last, my_idx;
+    };
+    auto tile_src = [&](int it, const unsigned char *idx_src) __attribute__((always_inline)) {
+        TileSrc t;
+        t.kt = k0 + (int64_t)it * kTileKeys;
+        t.last = (int)((k1 - t.kt) < kTileKeys ? (k1 - t.kt) : kTileKeys) - 1;
+        t.my_idx = 0;
+        if constexpr (IDX)
+            t.my_idx = it == 0 ? idx0 : clamp_row(reinterpret_cast<const int *>(idx_src + kIdxOff)[lane], a.n_kv);
+        t.base = IDX ? kvs : kvs + t.kt * a.kv_row_stride;
+        return t;
+    };
+    auto copy_aux = [&](const TileSrc &t, unsigned char *__restrict__ dst) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (mrow) {
+            const int r = ln < t.last ? ln : t.last;
+            const int64_t col = IDX ? (int64_t)shfl_int(t.my_idx, r) : t.kt + r;
+            __builtin_amdgcn_global_load_lds((const void *)(mrow + col), (LDS_PTR(void))(dst + kMaskOff), 2, 0, 0);
+        }
+        if constexpr (IDX) {                               // index entries of the tile after it
+            int64_t pos = t.kt + kTileKeys + ln;
+            if (pos >= k1) pos = k1 - 1;
+            __builtin_amdgcn_global_load_lds((const void *)(irow + pos), (LDS_PTR(void))(dst + kIdxOff), 4, 0, 0);
+        }
+    };
+    auto copy_one = [&](const TileSrc &t, int j, unsigned char *__restrict__ dst) __attribute__((always_inline)) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (j < kTileKeys / NW) {
+            const int r = wave + j * NW;
+            const int rc = r < t.last ? r : t.last;
+            const int64_t ri = IDX ? (int64_t)__builtin_amdgcn_readlane(t.my_idx, rc) : (int64_t)rc;
+            const uint8_t *rowp = t.base + ri * a.kv_row_stride;
+            __builtin_amdgcn_global_load_lds((const void *)(rowp + (uint32_t)(ln * 16)),
+                                             (LDS_PTR(void))(dst + r * kVRow), 16, 0, 0);
+        } else {
+            const int q = wave + (j - kTileKeys / NW) * NW;
+            const int r = 8 * q + (ln >> 3);
+            const int rc = r < t.last ? r : t.last;
+            const int chunk = (ln & 7) ^ ((r >> 1) & 7);
+            const int64_t ri = IDX ? (int64_t)shfl_int(t.my_idx, rc) : (int64_t)rc;
+            __builtin_amdgcn_global_load_lds((const void *)(t.base + ri * a.kv_row_stride + 1024 + 16 * chunk),
+                                             (LDS_PTR(void))(dst + kRopeOff + q * 1024), 16, 0, 0);
+        }
+    };
+
     // Dequantise a raw Q8_0 stage into the f16 tile (the 16-bit tile layout).  One task
     // = one 34-byte block of one row: f16 scale d at byte 0, 32 int8 codes after it;
     // value = code * d, computed exactly in fp32 (8-bit code x 11-bit d) and rounded
@@ -402,8 +461,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // LDS operands are loaded kQkD / kPvD steps ahead of the MFMAs that use them, and a
     // scheduling fence closes every step, so at most a few operands are in flight.
     constexpr int kQkD = 2, kPvD = 3;
-    auto compute_sub = [&](const unsigned char *stage, const unsigned char *mask_lds, int64_t kt, int sub0)
-        __attribute__((always_inline)) {
+    // hook(s) runs after the MFMAs of Q.K^T step s (copies placed among the steps).
+    auto compute_sub = [&](const unsigned char *stage, const unsigned char *mask_lds, int64_t kt, int sub0,
+                           auto &&hook) __attribute__((always_inline)) {
         const unsigned char *sb = stage + sub0 * kVRow;
         const unsigned char *rb = stage + kRopeOff + sub0 * 128;
         // S^T = K . Q^T: A = 16 keys x 32 dims from LDS (two 16-key blocks), B = Q
@@ -434,6 +494,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
                     sacc[kb][mb] = mfma16x16x32<KIND>(ka[s % (kQkD + 1)][kb], qreg[mb][s], sacc[kb][mb]);
+            hook(s);
             __builtin_amdgcn_sched_barrier(0);
         }
         // Scores in log2 units for this lane's 8 keys: i < 4: key sub0 + 4g + i; i >= 4: key
@@ -533,11 +594,22 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     // wave's copies, then a barrier, at the top of every iteration.
     auto step16 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur)
         __attribute__((always_inline)) {
-        if (it + 1 < n_tiles) issue_tile(it + 1, next, cur);
+        // With eight waves in key halves, the copies of tile it+1 ride on the Q.K^T steps
+        // (measured on decode: kernel -3 to -7%).  The 128-head prefill shape keeps the
+        // burst: spread there it ran 2.7% slower.
+        constexpr bool kSpread = NW == 8 && WK == 2;
+        static_assert(!kSpread || (kCopies == 9 && kQkD + 2 * kCopies <= 20), "one copy every other step");
+        const bool spread = kSpread && it >= 0 && it + 1 < n_tiles;
+        if (it + 1 < n_tiles && !spread) issue_tile(it + 1, next, cur);
         if (it < 0) return;
         const int64_t kt = k0 + (int64_t)it * kTileKeys;
+        const TileSrc t = tile_src(spread ? it + 1 : it, cur);
+        if (spread) copy_aux(t, next);
 #pragma unroll 1
-        for (int sub = kp; sub < 2; sub += WK) compute_sub(cur, cur + kMaskOff, kt, sub * kSub);
+        for (int sub = kp; sub < 2; sub += WK)
+            compute_sub(cur, cur + kMaskOff, kt, sub * kSub, [&](int s) __attribute__((always_inline)) {
+                if (spread && sub == kp && (s & 1) && (s >> 1) < kCopies) copy_one(t, s >> 1, next);
+            });
     };
     auto stepq8 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur,
                       unsigned char *__restrict__ f16tile) __attribute__((always_inline)) {
@@ -550,7 +622,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         __builtin_amdgcn_s_barrier();
         const int64_t kt = k0 + (int64_t)it * kTileKeys;
 #pragma unroll 1
-        for (int sub = kp; sub < 2; sub += WK) compute_sub(f16tile, cur + kMaskOff, kt, sub * kSub);
+        for (int sub = kp; sub < 2; sub += WK) compute_sub(f16tile, cur + kMaskOff, kt, sub * kSub, [](int) {});
     };
 
     // ---- main loop: one barrier per tile for 16-bit caches (it publishes tile `it`
