@@ -598,7 +598,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         // (measured on decode: kernel -3 to -7%).  The 128-head prefill shape keeps the
         // burst: spread there it ran 2.7% slower.
         constexpr bool kSpread = NW == 8 && WK == 2;
-        static_assert(!kSpread || (kCopies == 9 && kQkD + 2 * kCopies <= 20), "one copy every other step");
+        static_assert(!kSpread || 2 * kCopies <= 18, "one copy every other Q.K^T step");
         const bool spread = kSpread && it >= 0 && it + 1 < n_tiles;
         if (it + 1 < n_tiles && !spread) issue_tile(it + 1, next, cur);
         if (it < 0) return;
