@@ -82,8 +82,9 @@ int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type);
 
 /*
  * Workspace bytes a call with these sizes needs (0 when n_split resolves to 1).
- * n_split = 0 means the automatic choice.  The workspace holds the split partials
- * (fp32 m, l and unnormalised O per split, row and head) and is fully rewritten by
+ * n_split = 0 means the automatic choice.  The workspace holds the split partials (per
+ * split, row and head: fp32 m and l, and the unnormalised O as f16 values with an fp32
+ * power-of-two scale per 256-column half, 1040 bytes in all) and is fully rewritten by
  * every call; it needs no initialisation.
  */
 size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split);

@@ -727,10 +727,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             }
         }
     } else {
+        // this split's partial: m, l, and per 256-column half of O/l a scale and the
+        // scaled values in f16 (the layout partial_bytes describes)
         const int64_t RH = (int64_t)n_rows * a.n_head;
         float *wm = a.ws;
         float *wl = wm + (int64_t)a.n_split * RH;
-        float *wo = wl + (int64_t)a.n_split * RH;
+        float *wsc = wl + (int64_t)a.n_split * RH;                       // [split][row, head][half]
+        uint16_t *wo = reinterpret_cast<uint16_t *>(wsc + 2 * (int64_t)a.n_split * RH);
         const int64_t base = (int64_t)split * RH + (int64_t)row * a.n_head;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -741,13 +744,23 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             }
             if (n_tiles > 0) {              // an empty split leaves O unread by the merge
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int head = h_base + mb * 16 + 4 * g + r;
-                    if (head < a.n_head) {
-                        float *op = wo + (base + head) * kDV + l16;
+                for (int hf = 0; hf < 2; ++hf) {
+                    if (WK == 2 && hf != kp) continue;            // the other wave's half
 #pragma unroll
-                        for (int nb = 0; nb < 32; ++nb)
-                            if (owns(nb)) op[16 * nb] = o[mb][nb][r];
+                    for (int r = 0; r < 4; ++r) {
+                        float mx = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(o[mb][16 * hf + j][r]));
+                        const int e = partial_exp(group16_max(mx));
+                        const float sc = __builtin_amdgcn_ldexpf(1.f, 15 - e);
+                        const int head = h_base + mb * 16 + 4 * g + r;
+                        if (head < a.n_head) {
+                            uint16_t *op = wo + (base + head) * kDV + 256 * hf + l16;
+#pragma unroll
+                            for (int j = 0; j < 16; ++j)
+                                op[16 * j] = (uint16_t)pack_f16x2(o[mb][16 * hf + j][r] * sc, 0.f);
+                            if (l16 == 0) wsc[(base + head) * 2 + hf] = __builtin_amdgcn_ldexpf(1.f, e - 15);
+                        }
                     }
                 }
             }
@@ -1165,10 +1178,12 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
             }
         }
     } else {
+        // this split's partial, in the layout partial_bytes describes (wave d: half d)
         const int64_t RH = (int64_t)n_rows * a.n_head;
         float *wm = a.ws;
         float *wl = wm + (int64_t)a.n_split * RH;
-        float *wo = wl + (int64_t)a.n_split * RH;
+        float *wsc = wl + (int64_t)a.n_split * RH;
+        uint16_t *wo = reinterpret_cast<uint16_t *>(wsc + 2 * (int64_t)a.n_split * RH);
         const int64_t base = (int64_t)split * RH + (int64_t)row * a.n_head;
         const int head_l = h_base + 16 * d + l16;
         if (lane < 16 && head_l < a.n_head) {
@@ -1177,16 +1192,23 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
         }
         if (n_st > 0) {
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb)
+            for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int head = h_base + hb * 16 + 4 * g + r;
-                    if (head < a.n_head) {
-                        float *op = wo + (base + head) * kDV + 256 * d + l16;
+                    float mx = 0.f;
 #pragma unroll
-                        for (int nb = 0; nb < 16; ++nb) op[16 * nb] = o[hb][nb][r];
+                    for (int nb = 0; nb < 16; ++nb) mx = fmaxf(mx, fabsf(o[hb][nb][r]));
+                    const int e = partial_exp(group16_max(mx));
+                    const float sc = __builtin_amdgcn_ldexpf(1.f, 15 - e);
+                    if (head < a.n_head) {
+                        uint16_t *op = wo + (base + head) * kDV + 256 * d + l16;
+#pragma unroll
+                        for (int nb = 0; nb < 16; ++nb) op[16 * nb] = (uint16_t)pack_f16x2(o[hb][nb][r] * sc, 0.f);
+                        if (l16 == 0) wsc[(base + head) * 2 + d] = __builtin_amdgcn_ldexpf(1.f, e - 15);
                     }
                 }
+            }
         }
     }
 }
@@ -1194,10 +1216,13 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
 // Merge split partials: out = sum_i 2^(m_i - m*) O_i / sum_i 2^(m_i - m*) l_i; splits with
 // m_i = -inf (no kept key) weigh 0 and their O_i never contributes (it may be unwritten);
 // a row with no kept key anywhere outputs 0.  One workgroup per (row, head); thread t owns
-// dv quad t % 128 of splits t / 128, t / 128 + 4, ...  The partial O reads are the whole
-// cost, so they start first: each thread issues its first 8 loads, then (m_i, l_i) of all
-// splits are read in one round trip, reduced to the weights in LDS, and the loads already
-// in flight are weighted (a select drops unweighted splits); later batches follow, and
+// dv quad t % 128 of splits t / 128, t / 128 + 4, ...  O_i is stored as f16 values and a
+// power-of-two scale per 256-column half (see partial_bytes), so a split's factor for a
+// half is 2^(m_i - m*) times that scale.  The partial O reads are the whole cost, so they
+// start first: each thread issues its first 8 loads, then (m_i, l_i, scales) of all
+// splits are read in one round trip, reduced to the factors in LDS, and the loads already
+// in flight are weighted (a select drops unweighted splits, whose values are read but
+// may hold any bits); later batches follow, and
 // the four split groups are summed through LDS.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeGroups = kMergeThreads / 128;
@@ -1208,29 +1233,36 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
                                                               const float *__restrict__ sinks) {
     __shared__ float w_s[kMaxSplits];
     __shared__ float l_s[kMaxSplits];
+    __shared__ f32x2v sc_s[kMaxSplits];
     __shared__ float red[kMergeThreads / 64];
     __shared__ f32x4 part[kMergeGroups - 1][128];
     const int64_t rh = blockIdx.x;                    // row * n_head + head
     const int64_t RH = (int64_t)n_rows * n_head;
     const float *wm = ws;
     const float *wl = wm + (int64_t)n_split * RH;
-    const float *wo = wl + (int64_t)n_split * RH;
+    const f32x2v *wsc = reinterpret_cast<const f32x2v *>(wl + (int64_t)n_split * RH);
+    const uint16_t *wo = reinterpret_cast<const uint16_t *>(wsc + (int64_t)n_split * RH);
     const int tid = threadIdx.x;
     const int q = tid & 127, sg = tid >> 7;
-    const f32x4 *op = reinterpret_cast<const f32x4 *>(wo + rh * kDV) + q;
-    const int64_t step4 = RH * kDV / 4;               // f32x4 stride between splits
+    const u32x2 *op = reinterpret_cast<const u32x2 *>(wo + rh * kDV) + q;   // 4 f16 values
+    const int64_t step4 = RH * kDV / 4;               // stride between splits, in quads
+    // O of a split = scale of its half x the stored f16 values
+    auto f16x4_to_f32 = [](u32x2 v) __attribute__((always_inline)) {
+        return __builtin_convertvector(__builtin_bit_cast(f16x4v, v), f32x4);
+    };
 
-    f32x4 v0[kMergeBatch];
+    u32x2 v0[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
         const int i = sg + u * kMergeGroups;
-        v0[u] = i < n_split ? op[(int64_t)i * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
+        v0[u] = op[(int64_t)(i < n_split ? i : 0) * step4];   // unconditional: no wait until used
     }
     float mloc = -INFINITY;
     for (int i = tid; i < n_split; i += kMergeThreads) {
         const float mi = wm[i * RH + rh];
         w_s[i] = mi;
         l_s[i] = wl[i * RH + rh];
+        sc_s[i] = wsc[i * RH + rh];
         mloc = fmaxf(mloc, mi);
     }
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
@@ -1244,8 +1276,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     for (int i = tid; i < n_split; i += kMergeThreads) {
         const float mi = w_s[i];
         const float wgt = (mstar == -INFINITY || mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - mstar);
-        w_s[i] = wgt;
         if (wgt != 0.f) lloc += wgt * l_s[i];
+        // per-half factors of the stored values: weight x scale (0 for unweighted splits)
+        w_s[i] = wgt != 0.f ? wgt * sc_s[i][0] : 0.f;
+        l_s[i] = wgt != 0.f ? wgt * sc_s[i][1] : 0.f;
     }
     for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off);
     __syncthreads();
@@ -1257,28 +1291,33 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     if (sinks && mstar != -INFINITY)   // the sink joins the normaliser (m* in log2 units)
         lsum += __builtin_amdgcn_exp2f(sinks[rh % n_head] * 1.4426950408889634f - mstar);
 
+    const float *f_s = q < 64 ? w_s : l_s;           // this thread's half (uniform per wave)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
         const int i = sg + u * kMergeGroups;
-        const float wgt = i < n_split ? w_s[i] : 0.f;
-        if (wgt != 0.f) acc += wgt * v0[u];
+        const float wgt = i < n_split ? f_s[i] : 0.f;
+        const f32x4 x = f16x4_to_f32(v0[u]);
+        if (wgt != 0.f) acc += wgt * x;
     }
     int i = sg + kMergeBatch * kMergeGroups;
     for (; i + (kMergeBatch - 1) * kMergeGroups < n_split; i += kMergeBatch * kMergeGroups) {
-        f32x4 v[kMergeBatch];
+        u32x2 v[kMergeBatch];
         float wv[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
-            wv[u] = w_s[i + u * kMergeGroups];
-            v[u] = wv[u] != 0.f ? op[(int64_t)(i + u * kMergeGroups) * step4] : f32x4{0.f, 0.f, 0.f, 0.f};
+            wv[u] = f_s[i + u * kMergeGroups];
+            v[u] = op[(int64_t)(i + u * kMergeGroups) * step4];
         }
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) acc += wv[u] * v[u];
+        for (int u = 0; u < kMergeBatch; ++u) {   // unweighted splits may hold any bits: select
+            const f32x4 x = f16x4_to_f32(v[u]);
+            if (wv[u] != 0.f) acc += wv[u] * x;
+        }
     }
     for (; i < n_split; i += kMergeGroups) {
-        const float wgt = w_s[i];
-        if (wgt != 0.f) acc += wgt * op[(int64_t)i * step4];
+        const float wgt = f_s[i];
+        if (wgt != 0.f) acc += wgt * f16x4_to_f32(op[(int64_t)i * step4]);
     }
     if (sg > 0) part[sg - 1][q] = acc;
     __syncthreads();

@@ -35,6 +35,7 @@ __device__ __forceinline__ unsigned f32_to_bf16_bits(float x) {   // nearest eve
 
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // two floats -> two f16 (nearest even) in one register: one v_cvt_pk_f16_f32
@@ -70,6 +71,20 @@ __device__ __forceinline__ float wave_sum_groups(float x) {
     x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
     auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+// max over the 16 lanes of this lane's 16-lane group
+__device__ __forceinline__ float group16_max(float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Exponent e of a split partial's half: max |value| < 2^e (0 for an all-zero half; at
+// least -100, so that the scale 2^(15 - e) stays a normal float).
+__device__ __forceinline__ int partial_exp(float mx) {
+    const int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    return e < -100 ? -100 : e;
 }
 
 __device__ __forceinline__ int shfl_int(int v, int src_lane) {

@@ -54,8 +54,12 @@ constexpr int kMaxGridY = 65535;   // rows per launch (the grid's y extent)
 
 // Partial layout inside the workspace, for R = n_seq*n_tok rows, H heads, S splits:
 //   m [S][R][H] fp32 (log2 domain), l [S][R][H] fp32, o [S][R][H][512] fp32.
+// Split partials, per (split, row, head): m and l (fp32), two fp32 scales, and the
+// unnormalised O as 512 f16 values, each 256-column half stored times 2^(15 - e) where
+// max |O| < 2^e over the half (the scale kept is 2^(e - 15)).  Every value keeps f16's
+// relative precision (2^-11) whatever the magnitude of the cache's values.
 inline size_t partial_bytes(int64_t rows, int heads, int splits) {
-    return (size_t)splits * rows * heads * (2 + kDV) * sizeof(float);
+    return (size_t)splits * rows * heads * (4 * sizeof(float) + kDV * sizeof(uint16_t));
 }
 
 // Per-head attention with separate K (192 wide) and V (128 wide), 16-bit types.

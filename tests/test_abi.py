@@ -65,8 +65,8 @@ def test_workspace_and_splits(L):
     s = B.mla_fa_auto_splits(4, 128, 32768, B.MLA_FA_BF16)
     assert 1 < s <= 1024
     assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 1) == 0
-    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 8) == 8 * 4 * 128 * 514 * 4
-    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 0) == s * 4 * 128 * 514 * 4
+    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 8) == 8 * 4 * 128 * (4 * 4 + 512 * 2)
+    assert B.mla_fa_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 0) == s * 4 * 128 * (4 * 4 + 512 * 2)
     assert B.mla_fa_workspace_size(4, 100, 32768, B.MLA_FA_BF16, 8) == 0     # unsupported heads
 
 
