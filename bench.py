@@ -180,8 +180,13 @@ def _time_decode(B, p, copies, steps, warmup, n_split=0):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
 
+    cws = None
+    if sparse:      # the multi-workgroup compaction's chunk counts
+        cws = torch.empty(max(B.fa_mask_compact_workspace_size(p.n_seq, p.n_kv), 1), dtype=torch.uint8,
+                          device="cuda")
+
     def compact(i):
-        B.fa_mask_compact(mask, idx, cnt, stream=stream)
+        B.fa_mask_compact_ws(mask, idx, cnt, cws, stream=stream)
 
     def part(i):
         c = i % copies
@@ -233,11 +238,15 @@ def _time_decode_cold(B, p, calls=30):
     sparse = p.kind == "sparse"
     idx = torch.empty((p.n_seq, p.n_kv), dtype=torch.int32, device="cuda") if sparse else None
     cnt = torch.empty((p.n_seq,), dtype=torch.int32, device="cuda") if sparse else None
+    cws = None
+    if sparse:
+        cws = torch.empty(max(B.fa_mask_compact_workspace_size(p.n_seq, p.n_kv), 1), dtype=torch.uint8,
+                          device="cuda")
     flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")     # 512 MB
 
     def call():
         if sparse:
-            B.fa_mask_compact(mask, idx, cnt, stream=stream)
+            B.fa_mask_compact_ws(mask, idx, cnt, cws, stream=stream)
         B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, mask=mask, kv_idx=idx, kv_idx_count=cnt,
                         n_split=ns, workspace=ws, stream=stream)
 

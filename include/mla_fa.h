@@ -262,6 +262,25 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
 int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                     int32_t *idx, int64_t idx_row_stride, int32_t *count, void *stream);
 
+/*
+ * The same compaction (same result, bit for bit) spread over many workgroups per row,
+ * for rows of up to 2^22 cells whose rows start 16-byte aligned (mask 16-byte aligned,
+ * and mask_row_stride a multiple of 8 when n_rows > 1), and n_rows <= 65535.  Each row
+ * is cut into 4096-cell chunks: a first launch counts the kept cells of every chunk into
+ * the workspace; a second gives each chunk its output offset (the sum of the counts
+ * before it) and writes its cells.  The mask is read twice, by many CUs instead of one.
+ *   workspace   device, 4-byte aligned, at least fa_mask_compact_workspace_size(n_rows,
+ *               n_kv) bytes (the chunk counts; fully rewritten, no initialisation).
+ * Calls outside those limits run fa_mask_compact's kernel and leave the workspace
+ * untouched.  Errors as for fa_mask_compact, and ERR_WORKSPACE when the chunked form
+ * applies and the workspace is missing or short.  Calls that share a workspace on
+ * different streams race.
+ */
+size_t fa_mask_compact_workspace_size(int n_rows, int64_t n_kv);
+int fa_mask_compact_ws(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                       int32_t *idx, int64_t idx_row_stride, int32_t *count, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ MLA_FA_OK, MLA_FA_ERR_INVALID, MLA_FA_ERR_UNSUPPORTED, MLA_FA_ERR_WORKSPACE, MLA
 EXPORTS = ("mla_fa_strerror", "mla_fa_version", "mla_fa_auto_splits", "mla_fa_workspace_size",
            "mla_fa_decode", "mla_fa_decode_partials", "mla_fa_merge_partials", "mla_fa_prefill",
            "mla_fa_attend", "mla_fa_prefill_mha", "mla_fa_absorbed_workspace_size", "mla_fa_absorbed",
-           "fa_mask_compact")
+           "fa_mask_compact", "fa_mask_compact_workspace_size", "fa_mask_compact_ws")
 
 _LIB = None
 _p, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.mla_fa_prefill.argtypes = [_p, _i, _p, _i, _i64, _i, _i, _i64, _i, _p, _i64, _f, _p, _i, _p, _sz, _p]
         L.fa_mask_compact.restype = _i
         L.fa_mask_compact.argtypes = [_p, _i64, _i, _i64, _p, _i64, _p, _p]
+        L.fa_mask_compact_workspace_size.restype = _sz
+        L.fa_mask_compact_workspace_size.argtypes = [_i, _i64]
+        L.fa_mask_compact_ws.restype = _i
+        L.fa_mask_compact_ws.argtypes = [_p, _i64, _i, _i64, _p, _i64, _p, _p, _sz, _p]
         L.mla_fa_attend.restype = _i
         L.mla_fa_attend.argtypes = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64, _i64,
                                     _p, _p, _f, _f, _p, _i, _p, _sz, _p]
@@ -240,3 +244,16 @@ def fa_mask_compact(mask, idx, count, stream=None):
     n_rows, n_kv = mask.shape
     _check(lib().fa_mask_compact(_ptr(mask), mask.stride(0), n_rows, n_kv, _ptr(idx), idx.stride(0),
                                  _ptr(count), _stream(stream)), "fa_mask_compact")
+
+
+def fa_mask_compact_workspace_size(n_rows, n_kv):
+    return lib().fa_mask_compact_workspace_size(n_rows, n_kv)
+
+
+def fa_mask_compact_ws(mask, idx, count, workspace, stream=None):
+    """fa_mask_compact over many workgroups per row; `workspace` is a device tensor of at
+    least fa_mask_compact_workspace_size(n_rows, n_kv) bytes (or None where that is 0)."""
+    n_rows, n_kv = mask.shape
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_mask_compact_ws(_ptr(mask), mask.stride(0), n_rows, n_kv, _ptr(idx), idx.stride(0),
+                                    _ptr(count), _ptr(workspace), wsb, _stream(stream)), "fa_mask_compact_ws")

@@ -483,4 +483,31 @@ int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, i
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
+size_t fa_mask_compact_workspace_size(int n_rows, int64_t n_kv) {
+    if (n_rows < 1 || n_rows > kMaxGridY || n_kv < 1 || n_kv > 0x7FFFFFFFLL) return 0;
+    return (size_t)n_rows * (size_t)compact_chunks(n_kv) * sizeof(int32_t);
+}
+
+int fa_mask_compact_ws(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                       int32_t *idx, int64_t idx_row_stride, int32_t *count, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!mask || !idx || !count || n_rows < 1 || n_kv < 1 || n_kv > 0x7FFFFFFFLL)
+        return MLA_FA_ERR_INVALID;
+    if (!aligned(mask, 2) || !aligned(idx, 4) || !aligned(count, 4)) return MLA_FA_ERR_INVALID;
+    if (idx_row_stride < n_kv || (n_rows > 1 && mask_row_stride < n_kv) || mask_row_stride < 0)
+        return MLA_FA_ERR_INVALID;
+    const size_t need = fa_mask_compact_workspace_size(n_rows, n_kv);
+    const bool vec_rows = aligned(mask, 16) && (n_rows == 1 || mask_row_stride % 8 == 0);
+    hipError_t e;
+    if (need == 0 || !vec_rows) {     // the one-workgroup-per-row kernel; workspace untouched
+        e = launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
+                           static_cast<hipStream_t>(stream));
+    } else {
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 4)) return MLA_FA_ERR_WORKSPACE;
+        e = launch_compact_chunked(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
+                                   static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
+    }
+    return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -190,7 +190,127 @@ __global__ void __launch_bounds__(kWaves * 64) compact_kernel(const unsigned sho
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Multi-workgroup form, for callers that pass a workspace: the row is split into
+// kChunk-cell chunks, one workgroup of kCWaves waves each, so a row is read by many CUs
+// instead of one.  The same two passes as above, as two launches with the chunk counts
+// in the workspace between them: count each chunk's kept cells; then every chunk sums
+// the counts before it (its output offset), recounts its own cells, and writes them.
+// Each wave covers 1024 consecutive cells as two 512-cell steps (16 bytes per lane).
+constexpr int kChunk = 4096;
+constexpr int kCWaves = 4;
+static_assert(kChunk == kCWaves * 2 * 512, "two 512-cell steps per wave");
+
+// kept bits of this lane's 8 cells in each of the wave's two steps
+__device__ __forceinline__ void chunk_bits(const unsigned short *row, int64_t w0, int lane, int64_t n_kv,
+                                           unsigned &k0, unsigned &k1) {
+    k0 = kept_bits8(row, w0 + 8 * lane, n_kv);
+    k1 = kept_bits8(row, w0 + 512 + 8 * lane, n_kv);
+}
+
+// wave total of per-lane counts c in [0, 31]
+__device__ __forceinline__ unsigned wave_total5(unsigned c) {
+    unsigned t = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) t += (unsigned)__builtin_popcountll(__builtin_amdgcn_ballot_w64((c >> b) & 1u)) << b;
+    return t;
+}
+
+__global__ void __launch_bounds__(kCWaves * 64) chunk_count_kernel(const unsigned short *__restrict__ mask,
+                                                                   int64_t row_stride, int64_t n_kv, int n_chunks,
+                                                                   int32_t *__restrict__ ws) {
+    __shared__ unsigned wc[kCWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned short *row = mask + (int64_t)blockIdx.y * row_stride;
+    unsigned k0, k1;
+    chunk_bits(row, (int64_t)blockIdx.x * kChunk + wave * (kChunk / kCWaves), lane, n_kv, k0, k1);
+    const unsigned t = wave_total5(__builtin_popcount(k0) + __builtin_popcount(k1));
+    if (lane == 0) wc[wave] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned all = 0;
+#pragma unroll
+        for (int i = 0; i < kCWaves; ++i) all += wc[i];
+        ws[(int64_t)blockIdx.y * n_chunks + blockIdx.x] = (int32_t)all;
+    }
+}
+
+__global__ void __launch_bounds__(kCWaves * 64) chunk_write_kernel(const unsigned short *__restrict__ mask,
+                                                                   int64_t row_stride, int64_t n_kv, int n_chunks,
+                                                                   const int32_t *__restrict__ ws,
+                                                                   int32_t *__restrict__ idx, int64_t idx_stride,
+                                                                   int32_t *__restrict__ count) {
+    __shared__ unsigned red[2][kCWaves];
+    __shared__ unsigned wc[kCWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x;
+    const unsigned short *row = mask + (int64_t)blockIdx.y * row_stride;
+    const int32_t *cnt = ws + (int64_t)blockIdx.y * n_chunks;
+    // this chunk's kept bits (loads first), then the counts of the chunks before it
+    const int64_t w0 = (int64_t)c * kChunk + wave * (kChunk / kCWaves);
+    unsigned k0, k1;
+    chunk_bits(row, w0, lane, n_kv, k0, k1);
+    unsigned pre = 0, all = 0;
+    for (int i = threadIdx.x; i < n_chunks; i += kCWaves * 64) {
+        const unsigned v = (unsigned)cnt[i];
+        all += v;
+        pre += i < c ? v : 0u;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        pre += __shfl_xor(pre, off);
+        all += __shfl_xor(all, off);
+    }
+    const unsigned t = wave_total5(__builtin_popcount(k0) + __builtin_popcount(k1));
+    if (lane == 0) {
+        red[0][wave] = pre;
+        red[1][wave] = all;
+        wc[wave] = t;
+    }
+    __syncthreads();
+    unsigned offset = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kCWaves; ++i) {
+        offset += red[0][i] + (i < wave ? wc[i] : 0u);
+        total += red[1][i];
+    }
+    if (c == 0 && threadIdx.x == 0) count[blockIdx.y] = (int32_t)total;
+    int32_t *out = idx + (int64_t)blockIdx.y * idx_stride;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int64_t base = w0 + 512 * s + 8 * lane;
+        unsigned k = s == 0 ? k0 : k1;
+        unsigned below, tot;
+        wave_scan4(__builtin_popcount(k), below, tot);
+        unsigned pos = offset + below;
+        while (k) {
+            const int e = __builtin_ctz(k);
+            out[pos++] = (int32_t)(base + e);
+            k &= k - 1;
+        }
+        offset += tot;
+    }
+}
+
 }  // namespace
+
+int64_t compact_chunks(int64_t n_kv) {
+    return n_kv <= kCompactChunkedMax ? (n_kv + kChunk - 1) / kChunk : 0;
+}
+
+hipError_t launch_compact_chunked(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                                  int32_t *idx, int64_t idx_row_stride, int32_t *count, int32_t *ws,
+                                  hipStream_t stream) {
+    const int n_chunks = (int)compact_chunks(n_kv);
+    const auto *m = reinterpret_cast<const unsigned short *>(mask);
+    hipLaunchKernelGGL(chunk_count_kernel, dim3(n_chunks, n_rows), dim3(kCWaves * 64), 0, stream, m,
+                       mask_row_stride, n_kv, n_chunks, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_write_kernel, dim3(n_chunks, n_rows), dim3(kCWaves * 64), 0, stream, m,
+                       mask_row_stride, n_kv, n_chunks, ws, idx, idx_row_stride, count);
+    return hipGetLastError();
+}
 
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,

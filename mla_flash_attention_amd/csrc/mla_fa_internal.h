@@ -102,6 +102,13 @@ hipError_t launch_mha(const MhaArgs &a, int kv_kind, hipStream_t stream);
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,
                           hipStream_t stream);
+// Multi-workgroup compaction (rows of up to kCompactChunkedMax cells, 16-byte aligned):
+// compact_chunks(n_kv) int32 chunk counts per row of workspace; 0 = not available.
+constexpr int64_t kCompactChunkedMax = (int64_t)1 << 22;
+int64_t compact_chunks(int64_t n_kv);
+hipError_t launch_compact_chunked(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
+                                  int32_t *idx, int64_t idx_row_stride, int32_t *count, int32_t *ws,
+                                  hipStream_t stream);
 
 // Heads per workgroup of each shape.
 inline int shape_heads(int shape) {

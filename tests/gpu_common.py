@@ -37,8 +37,9 @@ def assert_parity(got, ref, what=""):
     return rel, mx
 
 
-def run_decode(p, n_split=0, out=None, ws=None, via_compaction=None):
-    """Run decode (dense, masked, or sparse through fa_mask_compact) for problem p.
+def run_decode(p, n_split=0, out=None, ws=None, via_compaction=None, chunked=False):
+    """Run decode (dense, masked, or sparse through fa_mask_compact, or through
+    fa_mask_compact_ws when `chunked`) for problem p.
     Returns (out fp32 numpy [n_seq*n_head][512], extras dict)."""
     import torch
     from mla_flash_attention_amd import binding as B
@@ -54,7 +55,12 @@ def run_decode(p, n_split=0, out=None, ws=None, via_compaction=None):
         assert mask is not None
         kv_idx = torch.full((p.n_seq, p.n_kv), -7, dtype=torch.int32, device="cuda")
         kv_cnt = torch.full((p.n_seq,), -7, dtype=torch.int32, device="cuda")
-        B.fa_mask_compact(mask, kv_idx, kv_cnt)
+        if chunked:
+            need = B.fa_mask_compact_workspace_size(p.n_seq, p.n_kv)
+            cws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            B.fa_mask_compact_ws(mask, kv_idx, kv_cnt, cws)
+        else:
+            B.fa_mask_compact(mask, kv_idx, kv_cnt)
         extras["idx"], extras["count"] = kv_idx, kv_cnt
     if ws is None:
         ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, n_split)

@@ -144,6 +144,27 @@ def test_compact_validation(L):
     assert f(m=FAKE + 1) == B.MLA_FA_ERR_INVALID
 
 
+def test_compact_ws_validation(L):
+    """The chunked compaction's argument checks (none of these launch anything)."""
+    assert B.fa_mask_compact_workspace_size(1, 131072) == 32 * 4
+    assert B.fa_mask_compact_workspace_size(3, 4097) == 3 * 2 * 4
+    assert B.fa_mask_compact_workspace_size(1, (1 << 22) + 1) == 0     # past the chunked limit
+    assert B.fa_mask_compact_workspace_size(0, 100) == 0
+    assert B.fa_mask_compact_workspace_size(70000, 100) == 0           # past the grid's y limit
+    f = lambda m=FAKE, ms=4096, rows=1, n=4096, idx=FAKE, istr=4096, cnt=FAKE, ws=FAKE, wsb=1 << 20: \
+        L.fa_mask_compact_ws(m, ms, rows, n, idx, istr, cnt, ws, wsb, None)
+    assert f(m=None) == B.MLA_FA_ERR_INVALID
+    assert f(idx=None) == B.MLA_FA_ERR_INVALID
+    assert f(cnt=None) == B.MLA_FA_ERR_INVALID
+    assert f(istr=4095) == B.MLA_FA_ERR_INVALID
+    assert f(rows=2, ms=100) == B.MLA_FA_ERR_INVALID
+    assert f(n=0) == B.MLA_FA_ERR_INVALID
+    assert f(m=FAKE + 1) == B.MLA_FA_ERR_INVALID
+    assert f(ws=None, wsb=0) == B.MLA_FA_ERR_WORKSPACE                  # the chunked form applies
+    assert f(wsb=3) == B.MLA_FA_ERR_WORKSPACE
+    assert f(ws=FAKE + 2) == B.MLA_FA_ERR_WORKSPACE                     # not 4-byte aligned
+
+
 def test_merge_validation(L):
     assert L.mla_fa_merge_partials(4, 128, 8, FAKE, None, 0, None) == B.MLA_FA_ERR_WORKSPACE
     assert L.mla_fa_merge_partials(4, 100, 8, FAKE, FAKE, 1 << 30, None) == B.MLA_FA_ERR_UNSUPPORTED

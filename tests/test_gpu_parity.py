@@ -50,9 +50,12 @@ def test_c4_full():
     assert_parity(got, oracle.attention_problem(p), "C4")
 
 
-def test_c5_full_sparse():
+@pytest.mark.parametrize("chunked", [False, True])
+def test_c5_full_sparse(chunked):
+    """The full sparse workload through either compaction entry point (the benchmark
+    times the chunked one)."""
     p = synth.make_config(5)
-    got, ex = run_decode(p)
+    got, ex = run_decode(p, chunked=chunked)
     idx_ref, cnt_ref = oracle.mask_compact(p.mask.reshape(1, -1))
     cnt = int(ex["count"].cpu()[0])
     assert cnt == int(cnt_ref[0])
@@ -201,9 +204,27 @@ def test_redzones_untouched():
 
 
 # ---------------------------------------------------------------- compaction
+def compact(mask, idx, cnt, entry):
+    """Run one compaction entry point; the chunked one gets a workspace between two
+    redzones, which must come back untouched."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    if entry == "one":
+        B.fa_mask_compact(mask, idx, cnt)
+        return
+    n_rows, n_kv = mask.shape
+    need = B.fa_mask_compact_workspace_size(n_rows, n_kv)
+    pad = 1024
+    wbuf = torch.full((need + 2 * pad,), 77, dtype=torch.uint8, device="cuda")
+    B.fa_mask_compact_ws(mask, idx, cnt, wbuf[pad:pad + need] if need else None)
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[:pad] == 77) and torch.all(wbuf[pad + need:] == 77)
+
+
+@pytest.mark.parametrize("entry", ["one", "chunked"])
 @pytest.mark.parametrize("case", ["empty", "full", "first", "last", "alternating", "runs", "tiny"])
 @pytest.mark.parametrize("aligned", [True, False])
-def test_compaction_cases(case, aligned):
+def test_compaction_cases(case, aligned, entry):
     import torch
     from mla_flash_attention_amd import binding as B
     n = 3 if case == "tiny" else 70001
@@ -232,7 +253,7 @@ def test_compaction_cases(case, aligned):
     mask = to_dev(host)[lead:].view(3, stride)[:, :n]
     idx = torch.full((3, n + 5), -9, dtype=torch.int32, device="cuda")
     cnt = torch.full((3,), -9, dtype=torch.int32, device="cuda")
-    B.fa_mask_compact(mask, idx, cnt)
+    compact(mask, idx, cnt, entry)
     torch.cuda.synchronize()
     idx_ref, cnt_ref = oracle.mask_compact(m)
     ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
@@ -262,6 +283,30 @@ def test_compaction_long_rows(n):
     ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
     assert np.array_equal(ci, cnt_ref)
     for r in range(2):
+        assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
+        assert np.all(ii[r, ci[r]:] == -9)
+
+
+@pytest.mark.parametrize("n", [1, 7, 4095, 4096, 4097, 8191, 131072, 131073, 1 << 22, (1 << 22) + 1])
+def test_compaction_chunked_sizes(n):
+    """The chunked compaction at and around its 4096-cell chunk boundaries, and on both
+    sides of its 2^22-cell limit (past it the one-workgroup kernel runs and the workspace
+    stays untouched); two rows of runs plus one fully kept row, bit-exact."""
+    import torch
+    g = np.random.default_rng(n + 11)
+    m = np.stack([synth.sparse_runs_mask(n, g, max_gap=900, max_run=300) for _ in range(2)]
+                 + [np.zeros(n, np.uint16)])
+    stride = n + 8 - n % 8
+    host = np.full(3 * stride, 0x1234, np.uint16)
+    host.reshape(3, stride)[:, :n] = m
+    mask = to_dev(host).view(3, stride)[:, :n]
+    idx = torch.full((3, n), -9, dtype=torch.int32, device="cuda")
+    cnt = torch.full((3,), -9, dtype=torch.int32, device="cuda")
+    compact(mask, idx, cnt, "chunked")
+    idx_ref, cnt_ref = oracle.mask_compact(m)
+    ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(ci, cnt_ref)
+    for r in range(3):
         assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]])
         assert np.all(ii[r, ci[r]:] == -9)
 

@@ -99,17 +99,23 @@ def test_random_compaction(case):
     host = np.full((n_rows, stride), 0x1234, np.uint16)
     host[:, :n] = m
     mask = to_dev(host)[:, :n]
-    idx = torch.full((n_rows, n), -9, dtype=torch.int32, device="cuda")
-    cnt = torch.full((n_rows,), -9, dtype=torch.int32, device="cuda")
-    B.fa_mask_compact(mask, idx, cnt)
-    torch.cuda.synchronize()
     idx_ref, cnt_ref = oracle.mask_compact(m)
-    ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
-    what = f"compaction case {case}: rows {n_rows} n {n} stride {stride} density {density}"
-    assert np.array_equal(ci, cnt_ref), what
-    for r in range(n_rows):
-        assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]]), what
-        assert np.all(ii[r, ci[r]:] == -9), what
+    for entry in ("one", "chunked"):
+        idx = torch.full((n_rows, n), -9, dtype=torch.int32, device="cuda")
+        cnt = torch.full((n_rows,), -9, dtype=torch.int32, device="cuda")
+        if entry == "one":
+            B.fa_mask_compact(mask, idx, cnt)
+        else:
+            need = B.fa_mask_compact_workspace_size(n_rows, n)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            B.fa_mask_compact_ws(mask, idx, cnt, ws)
+        torch.cuda.synchronize()
+        ci, ii = cnt.cpu().numpy(), idx.cpu().numpy()
+        what = f"compaction case {case} ({entry}): rows {n_rows} n {n} stride {stride} density {density}"
+        assert np.array_equal(ci, cnt_ref), what
+        for r in range(n_rows):
+            assert np.array_equal(ii[r, :ci[r]], idx_ref[r, :ci[r]]), what
+            assert np.all(ii[r, ci[r]:] == -9), what
 
 
 @pytest.mark.parametrize("case", range(N_CASES // 2))
