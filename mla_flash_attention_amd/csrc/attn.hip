@@ -317,7 +317,22 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             // A full tile of a packed cache (row stride 612) is one contiguous block in
             // memory too: copy it without splitting dwords into (row, column).
             const bool contiguous = !IDX && a.kv_row_stride == kQ8RowBytes && last == kTileKeys - 1;
-            if (contiguous) {
+            if (contiguous && (reinterpret_cast<uintptr_t>(tbase) & 15) == 0) {
+                // 16-byte copies: 38 KiB blocks and one 256-byte tail, a quarter of the
+                // copy instructions of the 4-byte form below
+                constexpr int kKiB = kQ8TileBytes / 1024;
+                static_assert(kQ8TileBytes - kKiB * 1024 == 256, "one 256-byte tail");
+#pragma unroll
+                for (int j = 0; j < (kKiB + NW - 1) / NW; ++j) {
+                    const int blk = wave + j * NW;
+                    if (blk < kKiB)
+                        __builtin_amdgcn_global_load_lds((const void *)(tbase + (uint32_t)(blk * 1024 + ln * 16)),
+                                                         (LDS_PTR(void))(dst + blk * 1024), 16, 0, 0);
+                }
+                if (wave == NW - 1)
+                    __builtin_amdgcn_global_load_lds((const void *)(tbase + (uint32_t)(kKiB * 1024 + ln * 4)),
+                                                     (LDS_PTR(void))(dst + kKiB * 1024), 4, 0, 0);
+            } else if (contiguous) {
 #pragma unroll
                 for (int j = 0; j < (kBlocks + NW - 1) / NW; ++j) {
                     const int blk = wave + j * NW;
@@ -613,6 +628,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     };
     auto stepq8 = [&](int it, unsigned char *__restrict__ next, const unsigned char *__restrict__ cur,
                       unsigned char *__restrict__ f16tile) __attribute__((always_inline)) {
+        // (The Q8_0 copies stay one burst: spread over the Q.K^T steps they made the
+        // compiler spill a Q register inside the loop, and the kernel ran 6% slower.)
         if (it + 1 < n_tiles) issue_tile(it + 1, next, cur);
         if (it < 0) return;
         dequant_tile(cur, f16tile);
