@@ -73,11 +73,12 @@ __device__ __forceinline__ float wave_sum_groups(float x) {
     return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
 }
 
-// max over the 16 lanes of this lane's 16-lane group
+// max over the 16 lanes of this lane's 16-lane group (DPP row rotations: VALU only)
 __device__ __forceinline__ float group16_max(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror:8
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));  // row_ror:2
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));  // row_ror:1
 }
 
 // Exponent e of a split partial's half: max |value| < 2^e (0 for an all-zero half; at
