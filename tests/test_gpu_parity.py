@@ -203,6 +203,39 @@ def test_redzones_untouched():
     assert torch.all(wbuf[:pad] == 77) and torch.all(wbuf[-pad:] == 77)
 
 
+def _scale_bits(bits, shift, type_id):
+    """Multiply 16-bit floats (bits) by 2^shift exactly, by moving the exponent field of
+    every normal value (zeros stay zero); asserts nothing leaves the normal range."""
+    mant = 7 if type_id == BF16 else 10
+    emax = 255 if type_id == BF16 else 31
+    v = bits.astype(np.int64)
+    e = (v >> mant) & emax
+    ok = (e > 0) & (e < emax)
+    e2 = e + shift
+    assert np.all((e2[ok] > 0) & (e2[ok] < emax))
+    v = np.where(ok, (v & ~(emax << mant)) | (e2 << mant), v)
+    return v.astype(np.uint16)
+
+
+@pytest.mark.parametrize("t,shift", [(BF16, 90), (BF16, -90), (BF16, 40)])
+def test_split_partials_value_range(t, shift):
+    """Split partials hold O in f16 under a power-of-two scale per half: outputs far from
+    1 in magnitude must keep their precision.  The cache's latent dims (K and V) are
+    scaled by 2^shift and Q's latent dims by 2^-shift, which leaves every score exactly
+    as it was and scales the output by exactly 2^shift (bf16 only: f16's exponent range
+    cannot move N(0,1) values this far)."""
+    p = synth.make_problem(kind="decode", n_seq=2, n_head=128, n_kv=3000, q_type=t, kv_type=t, seed=77)
+    ref = oracle.attention_problem(p)
+    kv = p.kv.copy()
+    kv[..., :512] = _scale_bits(kv[..., :512], shift, t)
+    q = p.q.copy()
+    q[..., :512] = _scale_bits(q[..., :512], -shift, t)
+    p.kv, p.q = kv, q
+    got, _ = run_decode(p, n_split=8)
+    assert np.all(np.isfinite(got))
+    assert_parity(got * 2.0 ** -shift, ref, f"value range 2^{shift}")
+
+
 # ---------------------------------------------------------------- compaction
 def compact(mask, idx, cnt, entry):
     """Run one compaction entry point; the chunked one gets a workspace between two
