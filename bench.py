@@ -533,6 +533,7 @@ def main():
             r = _time_decode(B, p, 1, args.steps, args.warmup)
             cells, kb, cb, fl = _algo_decode(p, kept=r["kept"])
             sec["c5_sparse_131072_cells"] = dict(ms=r["step_ms"], compact_ms=r["compact_ms"],
+                                                 compaction="fa_mask_compact_ws (4096-cell chunks)",
                                                  attn_ms=r["part_ms"], merge_ms=r["merge_ms"],
                                                  kept=r["kept"], n_split=r["n_split"],
                                                  scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
