@@ -8,7 +8,7 @@ every input already resident in HBM.  Timed steps rotate over 4 copies of the in
 HBM.  Prints one JSON line (see the repository's bench contract).
 
 Secondary lines (same JSON object, key "secondary"): the other workloads - 16-head
-f16 decode (warm, and cold: caches flushed before each call), 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells (warm and cold),
+f16 decode (warm, and cold: caches flushed before each call), 2048-token causal prefill, Q8_0 decode, sparse decode at 131072 cells (bf16 warm and cold, Q8_0 warm),
 ragged 2-token decode, per-head (DK=192 / DV=128) prefill, and decode with the absorbed
 W_UK / W_UV projections either side.
 
@@ -57,6 +57,8 @@ def _args():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
                          "--copy-calibration into profiles/hbm_traffic.json and exit")
+    ap.add_argument("--traffic-key", default="decode_c2",
+                    help="workload the --traffic-from runs timed (decode_c2, decode_c4_q8_0)")
     return ap.parse_args()
 
 
@@ -70,11 +72,16 @@ def _counter_rows(d):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir):
+def write_traffic(fetch_dir, write_dir, key):
     """HBM bytes per launch of the split-attention kernel from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for a 1 GiB device
-    copy (copy reads 1 GiB and writes 1 GiB)."""
+    copy (copy reads 1 GiB and writes 1 GiB); stored under `key` (the workload the two
+    counter runs timed) in profiles/hbm_traffic.json."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     out = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            out = json.load(f)
     per = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
@@ -87,14 +94,13 @@ def write_traffic(fetch_dir, write_dir):
         factor = (1 << 30) / (max(copy) * 1024.0)    # bytes per counted KiB
         per[name] = dict(kib_per_launch=float(np.median(attn)), copy_kib=max(copy), factor=factor,
                          bytes_per_launch=float(np.median(attn)) * 1024.0 * factor)
-    out["decode_c2"] = dict(source_hash=_source_hash(),
+    out[key] = dict(source_hash=_source_hash(),
                             bytes_per_launch=per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"],
                             read_bytes=per["FETCH_SIZE"]["bytes_per_launch"],
                             write_bytes=per["WRITE_SIZE"]["bytes_per_launch"], counters=per)
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    print(json.dumps(out[key], indent=1))
 
 
 def _dev(a):
@@ -376,6 +382,26 @@ def _algo_decode(p, kept=None):
     return cells, kernel_bytes, call_bytes, flops
 
 
+def _sparse_line(p, r):
+    """The sparse decode step and its three launches, each with its HBM fraction:
+    compaction (2 B of mask read per scanned cell, 4 B of index written per kept cell),
+    attention (kept rows + Q), merge (the split partials read, the output written)."""
+    kept, ns = r["kept"], r["n_split"]
+    cells, kb, cb, fl = _algo_decode(p, kept=kept)
+    partial_bytes = ns * p.n_seq * p.n_head * (16 + 512 * 2)
+    compact_bytes = 2 * p.n_kv * p.n_seq + 4 * cells + 4 * p.n_seq
+    merge_bytes = partial_bytes + p.n_seq * p.n_head * 512 * 4
+    frac = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return dict(ms=r["step_ms"], compact_ms=r["compact_ms"], compaction="fa_mask_compact_ws (4096-cell chunks)",
+                attn_ms=r["part_ms"], merge_ms=r["merge_ms"], kept=kept, n_split=ns,
+                kept_row_bytes=cells * ROW_BYTES[p.kv_type], partial_bytes=partial_bytes,
+                scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
+                kept_cells_per_s=kept / (r["step_ms"] * 1e-3),
+                hbm_frac={"compaction": frac(compact_bytes, r["compact_ms"]), "attention": frac(kb, r["part_ms"]),
+                          "merge": frac(merge_bytes, r["merge_ms"]) if r["merge_ms"] else None,
+                          "step": frac(cb, r["step_ms"])})
+
+
 def _measured_peaks(torch, reps=5):
     """What this GPU measurably delivers (libmlapeaks, include/mla_peaks.h): HBM stream
     read of 4 GiB (past the 256 MB last-level cache), dense bf16 MFMA issue, and LDS
@@ -430,7 +456,7 @@ def _cpu_baseline(p, limit_s=40.0):
 def main():
     args = _args()
     if args.traffic_from:
-        write_traffic(*args.traffic_from)
+        write_traffic(*args.traffic_from, args.traffic_key)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -524,20 +550,24 @@ def main():
             r = _time_decode(B, p, args.copies, args.steps, args.warmup)
             cells, kb, cb, fl = _algo_decode(p)
             tf = fl / (r["part_ms"] * 1e-3) / 1e12
+            # the Q8_0 kernel computes with f16 MFMA operands: its bound is the f16 peak
+            # (the same 2.5 PFLOP/s dense as bf16); HBM is the secondary fraction
             sec["c4_decode_q8_0"] = dict(ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3),
                                          kernel_ms=r["part_ms"], merge_ms=r["merge_ms"], n_split=r["n_split"],
                                          hbm_frac=kb / (r["part_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                         mfma_tflops=tf, mfma_frac=tf / MFMA_BF16_PEAK_TFLOPS)
-        if want("c5"):
-            p = synth.make_config(5)
+                                         roofline={"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                                   "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                                   "traffic": _traffic("decode_c4_q8_0"),
+                                                   "kernel": "attn_kernel (Q8_0, split attention)",
+                                                   "algorithmic_flops": fl, "algorithmic_bytes": kb})
+        for tag, kvt in (("c5_sparse_131072_cells", synth.TYPE_BF16), ("c5_q8_0_sparse_131072_cells", synth.TYPE_Q8_0)):
+            if not want("c5"):
+                break
+            p = synth.make_config(5, kv_type=kvt)
             r = _time_decode(B, p, 1, args.steps, args.warmup)
-            cells, kb, cb, fl = _algo_decode(p, kept=r["kept"])
-            sec["c5_sparse_131072_cells"] = dict(ms=r["step_ms"], compact_ms=r["compact_ms"],
-                                                 compaction="fa_mask_compact_ws (4096-cell chunks)",
-                                                 attn_ms=r["part_ms"], merge_ms=r["merge_ms"],
-                                                 kept=r["kept"], n_split=r["n_split"],
-                                                 scanned_cells_per_s=p.n_kv / (r["step_ms"] * 1e-3),
-                                                 kept_cells_per_s=r["kept"] / (r["step_ms"] * 1e-3))
+            sec[tag] = _sparse_line(p, r)
+            if kvt != synth.TYPE_BF16:
+                continue
             rc = _time_decode_cold(B, p)
             sec["c5_sparse_131072_cells_cold"] = dict(ms=rc["ms"], p10=rc["p10"], p90=rc["p90"],
                                                       scanned_cells_per_s=p.n_kv / (rc["ms"] * 1e-3))

@@ -34,8 +34,16 @@
  *   - Element types: q is f16 or bf16 (bits, [..][n_head][576] contiguous); the
  *     cache is f16, bf16 or Q8_0.  Supported pairs: f16/f16, bf16/bf16, f16/Q8_0,
  *     bf16/Q8_0.  A Q8_0 row is 18 blocks of {f16 scale d, 32 int8 codes} = 612
- *     bytes; value = code * d.  Q8_0 is computed in f16 on the GPU, f16 caches in
- *     f16 and bf16 caches in bf16, all with fp32 accumulation.
+ *     bytes; value = code * d.  f16 caches are computed in f16 and bf16 caches in
+ *     bf16, with fp32 accumulation.
+ *   - Q8_0 range contract: Q8_0 caches are computed with f16 operands.  Each cache
+ *     value is f16(code * d), rounded once and saturated to +-65504, and a bf16 query
+ *     is converted to f16 with the same saturation (values below f16's subnormal
+ *     range become 0).  So the result is the exact one whenever |code * d| <= 65504
+ *     (always when |d| < 512: 128 * 511.75 = 65504; a block quantised from values in
+ *     f16 range has d <= 516, where only 127 * d may pass 65504, by under 0.05%) and
+ *     the query lies within f16's range.  Past that, values are clamped, never
+ *     infinite; d must be finite.
  *   - n_head is a multiple of 16 in [16, 128].  Query rows (n_seq * n_tok) times
  *     n_head is at most 2^31 - 1; more is MLA_FA_ERR_INVALID.  Any number of rows
  *     within that runs: calls beyond 65535 rows are issued as several launches.
@@ -45,6 +53,10 @@
  *     count of automatic plans; MLA_FA_SHAPE=16|32|64|128|p64|p128 forces the
  *     heads-per-workgroup shape; MLA_FA_LOG (any value) prints each call's plan to
  *     stderr.
+ *   - Test hook, read at each call: with MLA_FA_FAIL_LAUNCH=<k> (k >= 1) a call
+ *     launches no kernel at all; it walks its launch sequence and reports its k-th
+ *     launch as failed (MLA_FA_ERR_HIP), or MLA_FA_OK when it has fewer launches.  It
+ *     exists so that every launch-error return can be tested without a GPU.
  */
 #ifndef MLA_FA_H
 #define MLA_FA_H
@@ -69,7 +81,8 @@ enum mla_fa_status {
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *mla_fa_strerror(int status);
 
-/* Library version as major*10000 + minor*100 + patch. */
+/* Library version as major*10000 + minor*100 + patch (2.0.0: mla_fa_attend takes
+ * per-token sparse index lists). */
 int mla_fa_version(void);
 
 /*
@@ -157,8 +170,10 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
  * softcap, ALiBi slopes and attention sinks that the Metal tensor-API flash-attention
  * kernel supports for the 576/512 shape ("llama.cpp Metal: tensor-API flash attention
  * for F16 KV caches" news item; the pages name the features, the readings below are
- * the plain ones).  mla_fa_decode is the special case n_tok = 1, kv_len = NULL,
- * causal = 0 and no extras (less the sparse index path, which only it offers).
+ * the plain ones), and sparse attention over one compacted index list per query token
+ * ("llama.cpp Vulkan backend adds sparse Flash Attention for quantized K/V": one mask
+ * row per query, compacted, feeding the sparse attention).  mla_fa_decode is the
+ * special case n_tok = 1, kv_len = NULL, causal = 0 and no extras.
  *   q        [n_seq][n_tok][n_head][576] f16/bf16 bits (device).
  *   kv       row j of sequence s at kv + s*kv_seq_stride + j*kv_row_stride (bytes);
  *            n_kv rows of capacity per sequence; alignment as for decode.
@@ -169,6 +184,16 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
  *            requires n_tok <= n_kv.
  *   mask     NULL, or f16 bits, element (s, t, j) at s*mask_seq_stride +
  *            t*mask_tok_stride + j: -inf drops the cell, other values add to the score.
+ *   kv_idx   NULL for dense rows.  Otherwise the sparse path: row (s, t) attends only to
+ *   kv_idx_count  the cells kv_idx[s*idx_seq_stride + t*idx_tok_stride + c] for
+ *   idx_seq_stride, idx_tok_stride   c < kv_idx_count[s*n_tok + t], an ascending list
+ *            as fa_mask_compact writes for the n_seq*n_tok mask rows (device arrays,
+ *            int32, 4-byte aligned; the counts are read on the device).  The mask, if
+ *            given, is still added at the gathered cells.  Entries must lie in
+ *            [0, n_kv) (the kernels clamp any that do not; the result is then
+ *            unspecified).  Requires causal = 0 and kv_len = NULL: the list alone says
+ *            which cells a row sees.  Strides are elements, each at least n_kv where
+ *            more than one sequence / token uses it.
  *   alibi_slopes NULL, or fp32 [n_head] (device): the bias of a kept cell for head h is
  *            alibi_slopes[h] times its mask value (dropped cells stay dropped).
  *   sinks    NULL, or fp32 [n_head] (device): a per-head logit that joins the softmax
@@ -177,15 +202,16 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
  *            softcap * tanh(x / softcap) before the mask bias is added.
  *   out      [n_seq][n_tok][n_head][512] fp32 (device).
  *   n_split / workspace as for decode with n_rows = n_seq * n_tok.
- * Errors: as for decode; ERR_INVALID also for a negative or non-finite softcap and for
- * kv_len / alibi_slopes / sinks not 4-byte aligned.
+ * Errors: as for decode; ERR_INVALID also for a negative or non-finite softcap, for
+ * kv_len / alibi_slopes / sinks not 4-byte aligned, and for kv_idx with causal or kv_len.
  */
 int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
                   int64_t kv_seq_stride, int n_seq, int n_tok, int n_head, int64_t n_kv,
                   const int32_t *kv_len, int causal, const uint16_t *mask, int64_t mask_seq_stride,
-                  int64_t mask_tok_stride, const float *alibi_slopes, const float *sinks, float softcap,
-                  float scale, float *out, int n_split, void *workspace, size_t workspace_bytes,
-                  void *stream);
+                  int64_t mask_tok_stride, const int32_t *kv_idx, const int32_t *kv_idx_count,
+                  int64_t idx_seq_stride, int64_t idx_tok_stride, const float *alibi_slopes,
+                  const float *sinks, float softcap, float scale, float *out, int n_split, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 /*
  * Per-head attention with separate keys and values: the non-absorbed MLA shape, where

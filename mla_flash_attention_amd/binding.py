@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
         L.fa_mask_compact_ws.argtypes = [_p, _i64, _i, _i64, _p, _i64, _p, _p, _sz, _p]
         L.mla_fa_attend.restype = _i
         L.mla_fa_attend.argtypes = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i, _i64, _p, _i, _p, _i64, _i64,
-                                    _p, _p, _f, _f, _p, _i, _p, _sz, _p]
+                                    _p, _p, _i64, _i64, _p, _p, _f, _f, _p, _i, _p, _sz, _p]
         L.mla_fa_absorbed_workspace_size.restype = _sz
         L.mla_fa_absorbed_workspace_size.argtypes = [_i, _i, _i64, _i, _i]
         L.mla_fa_absorbed.restype = _i
@@ -177,20 +177,24 @@ def mla_fa_prefill(q, q_type, kv, kv_type, scale, out, *, causal=True, mask=None
 
 
 def mla_fa_attend(q, q_type, kv, kv_type, scale, out, *, kv_len=None, causal=False, mask=None,
-                  alibi=None, sinks=None, softcap=0.0, n_split=0, workspace=None, stream=None):
+                  kv_idx=None, kv_idx_count=None, alibi=None, sinks=None, softcap=0.0, n_split=0,
+                  workspace=None, stream=None):
     """q [n_seq][n_tok][n_head][576], kv [n_seq][n_kv][row] (n_kv = capacity), out fp32
     [n_seq][n_tok][n_head][512]; kv_len int32 [n_seq]; mask [n_seq][n_tok][>=n_kv] f16
-    bits; alibi / sinks fp32 [n_head]; softcap 0 = off."""
+    bits; kv_idx int32 [n_seq][n_tok][>=n_kv] + kv_idx_count int32 [n_seq][n_tok] for the
+    sparse path; alibi / sinks fp32 [n_head]; softcap 0 = off."""
     n_seq, n_tok, n_head = q.shape[0], q.shape[1], q.shape[2]
     n_kv = kv.shape[-2]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mseq = 0 if mask is None else mask.stride(0)
     mtok = 0 if mask is None else mask.stride(1)
+    iseq = 0 if kv_idx is None else kv_idx.stride(0)
+    itok = 0 if kv_idx is None else kv_idx.stride(1)
     _check(lib().mla_fa_attend(_ptr(q), q_type, _ptr(kv), kv_type, _row_stride_bytes(kv),
                                _seq_stride_bytes(kv, n_seq), n_seq, n_tok, n_head, n_kv, _ptr(kv_len),
-                               1 if causal else 0, _ptr(mask), mseq, mtok, _ptr(alibi), _ptr(sinks),
-                               float(softcap), float(scale), _ptr(out), n_split, _ptr(workspace), ws_bytes,
-                               _stream(stream)),
+                               1 if causal else 0, _ptr(mask), mseq, mtok, _ptr(kv_idx), _ptr(kv_idx_count),
+                               iseq, itok, _ptr(alibi), _ptr(sinks), float(softcap), float(scale), _ptr(out),
+                               n_split, _ptr(workspace), ws_bytes, _stream(stream)),
            "mla_fa_attend")
     return out
 

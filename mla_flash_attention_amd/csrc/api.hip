@@ -17,6 +17,26 @@ constexpr int kMinTilesPerSplit = 1;   // short caches: one tile per split is fa
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Failure injection for tests of the launch-error path.  With MLA_FA_FAIL_LAUNCH=<k> in
+// the environment, an entry point launches nothing: it walks its launch sequence and
+// reports its k-th launch (1-based) as failed, so every MLA_FA_ERR_HIP return can be
+// reached without a GPU.  Read once per call; thread-local, so concurrent calls on other
+// threads keep their own count.
+thread_local int t_launch_no = 0, t_fail_at = 0;
+void begin_call() {
+    t_launch_no = 0;
+    const char *e = std::getenv("MLA_FA_FAIL_LAUNCH");
+    t_fail_at = e && *e ? std::atoi(e) : 0;
+}
+// Whether the next launch is to be skipped; *failed says whether it reports failure.
+bool launch_skipped(bool *failed) {
+    ++t_launch_no;
+    *failed = t_launch_no == t_fail_at;
+    return t_fail_at > 0;
+}
+// hipSuccess / a launch error for a launch the test hook skipped.
+hipError_t skipped_status(bool failed) { return failed ? hipErrorLaunchFailure : hipSuccess; }
+
 int kv_kind_of(int kv_type) {
     return kv_type == MLA_FA_BF16 ? KV_BF16 : kv_type == MLA_FA_F16 ? KV_F16 : KV_Q8;
 }
@@ -116,6 +136,7 @@ struct Common {
     int64_t mask_seq_stride, mask_tok_stride;
     const int32_t *kv_idx, *kv_idx_count;
     int64_t idx_seq_stride;
+    int64_t idx_tok_stride = 0;
     float scale;
     float *out;
     int n_split;
@@ -155,9 +176,12 @@ int validate(const Common &c) {
     if (!aligned(c.kv_len, 4) || !aligned(c.alibi, 4) || !aligned(c.sinks, 4)) return MLA_FA_ERR_INVALID;
     if ((c.kv_idx == nullptr) != (c.kv_idx_count == nullptr)) return MLA_FA_ERR_INVALID;
     if (c.kv_idx) {
-        if (c.n_tok != 1 || c.causal) return MLA_FA_ERR_INVALID;
+        // an index list says which cells its row sees: no causal edge or valid lengths on top
+        if (c.causal || c.kv_len) return MLA_FA_ERR_INVALID;
         if (!aligned(c.kv_idx, 4) || !aligned(c.kv_idx_count, 4)) return MLA_FA_ERR_INVALID;
-        if (c.idx_seq_stride < 1 || (c.n_seq > 1 && c.idx_seq_stride < c.n_kv)) return MLA_FA_ERR_INVALID;
+        if (c.idx_seq_stride < 0 || c.idx_tok_stride < 0) return MLA_FA_ERR_INVALID;
+        if ((c.n_seq > 1 && c.idx_seq_stride < c.n_kv) || (c.n_tok > 1 && c.idx_tok_stride < c.n_kv))
+            return MLA_FA_ERR_INVALID;
     }
     return MLA_FA_OK;
 }
@@ -181,6 +205,7 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
     a.kv_idx = c.kv_idx;
     a.kv_idx_count = c.kv_idx_count;
     a.idx_seq_stride = c.idx_seq_stride;
+    a.idx_tok_stride = c.idx_tok_stride;
     a.out = c.out;
     a.ws = static_cast<float *>(c.ws);
     a.n_kv = c.n_kv;
@@ -203,7 +228,8 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
         fprintf(stderr, "mla_fa: rows=%lld heads=%d n_kv=%lld split=%d chunk=%lld shape=%d hg=%d grid=%dx%lld\n",
                 (long long)n_rows, c.n_head, (long long)c.n_kv, p.n_split, (long long)p.split_chunk,
                 p.shape, p.head_groups, p.grid_x, (long long)n_rows);
-    hipError_t e = launch_attention(a, kv_kind_of(c.kv_type), p.shape, stream);
+    bool fail;
+    hipError_t e = launch_skipped(&fail) ? skipped_status(fail) : launch_attention(a, kv_kind_of(c.kv_type), p.shape, stream);
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -213,8 +239,10 @@ int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *w
     if (n_rows * n_head > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;   // one merge workgroup per (row, head)
     const size_t need = partial_bytes(n_rows, n_head, n_split);
     if (!ws || ws_bytes < need || !aligned(ws, 16)) return MLA_FA_ERR_WORKSPACE;
-    hipError_t e = launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws), out, sinks,
-                                stream);
+    bool fail;
+    hipError_t e = launch_skipped(&fail) ? skipped_status(fail)
+                                         : launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws),
+                                                        out, sinks, stream);
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -231,6 +259,11 @@ Common decode_common(const void *q, int q_type, const void *kv, int kv_type, int
     c.kv_idx = kv_idx; c.kv_idx_count = kv_idx_count; c.idx_seq_stride = idx_seq_stride;
     c.scale = scale; c.out = out; c.n_split = n_split; c.ws = ws; c.ws_bytes = ws_bytes;
     return c;
+}
+
+hipError_t run_proj(const ProjArgs &pa, int kind, bool a_f32, bool c_f32, hipStream_t s) {
+    bool fail;
+    return launch_skipped(&fail) ? skipped_status(fail) : launch_proj(pa, kind, a_f32, c_f32, s);
 }
 
 // Workspace of mla_fa_absorbed: the 576-wide queries (16-bit), the latent outputs (fp32)
@@ -263,7 +296,7 @@ const char *mla_fa_strerror(int status) {
     return "unknown status";
 }
 
-int mla_fa_version(void) { return 10000; }
+int mla_fa_version(void) { return 20000; }
 
 int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type) {
     if (n_rows < 1 || n_kv < 1 || check_heads(n_head)) return 1;
@@ -282,6 +315,7 @@ int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_typ
                            const int32_t *kv_idx, const int32_t *kv_idx_count,
                            int64_t idx_seq_stride, float scale, float *out, int n_split,
                            void *workspace, size_t workspace_bytes, void *stream) {
+    begin_call();
     Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
                              mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
                              n_split, workspace, workspace_bytes);
@@ -293,6 +327,7 @@ int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_typ
 
 int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const void *workspace,
                           size_t workspace_bytes, void *stream) {
+    begin_call();
     if (!out || n_rows < 1 || n_split < 1 || n_split > kMaxSplits || !aligned(out, 16))
         return MLA_FA_ERR_INVALID;
     int st = check_heads(n_head);
@@ -306,6 +341,7 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
                   const uint16_t *mask, int64_t mask_seq_stride, const int32_t *kv_idx,
                   const int32_t *kv_idx_count, int64_t idx_seq_stride, float scale, float *out,
                   int n_split, void *workspace, size_t workspace_bytes, void *stream) {
+    begin_call();
     Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
                              mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
                              n_split, workspace, workspace_bytes);
@@ -324,6 +360,7 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
                    int n_tok, int n_head, int64_t n_kv, int causal, const uint16_t *mask,
                    int64_t mask_row_stride, float scale, float *out, int n_split,
                    void *workspace, size_t workspace_bytes, void *stream) {
+    begin_call();
     Common c;
     c.q = q; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
     c.kv_row_stride = kv_row_stride; c.kv_seq_stride = 0;
@@ -345,15 +382,18 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
 int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
                   int64_t kv_seq_stride, int n_seq, int n_tok, int n_head, int64_t n_kv,
                   const int32_t *kv_len, int causal, const uint16_t *mask, int64_t mask_seq_stride,
-                  int64_t mask_tok_stride, const float *alibi_slopes, const float *sinks, float softcap,
-                  float scale, float *out, int n_split, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+                  int64_t mask_tok_stride, const int32_t *kv_idx, const int32_t *kv_idx_count,
+                  int64_t idx_seq_stride, int64_t idx_tok_stride, const float *alibi_slopes,
+                  const float *sinks, float softcap, float scale, float *out, int n_split, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    begin_call();
     Common c;
     c.q = q; c.q_type = q_type; c.kv = kv; c.kv_type = kv_type;
     c.kv_row_stride = kv_row_stride; c.kv_seq_stride = kv_seq_stride;
     c.n_seq = n_seq; c.n_tok = n_tok; c.n_head = n_head; c.n_kv = n_kv; c.causal = causal;
     c.mask = mask; c.mask_seq_stride = mask_seq_stride; c.mask_tok_stride = mask_tok_stride;
-    c.kv_idx = nullptr; c.kv_idx_count = nullptr; c.idx_seq_stride = 0;
+    c.kv_idx = kv_idx; c.kv_idx_count = kv_idx_count; c.idx_seq_stride = idx_seq_stride;
+    c.idx_tok_stride = idx_tok_stride;
     c.scale = scale; c.out = out; c.n_split = n_split; c.ws = workspace; c.ws_bytes = workspace_bytes;
     c.kv_len = kv_len; c.alibi = alibi_slopes; c.sinks = sinks; c.softcap = softcap;
     int st = validate(c);
@@ -372,6 +412,7 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
                        int64_t k_row_stride, int64_t v_row_stride, int n_tok, int n_head, int64_t n_kv,
                        int causal, const uint16_t *mask, int64_t mask_row_stride, float scale,
                        float *out, void *stream) {
+    begin_call();
     if (!q || !k || !v || !out) return MLA_FA_ERR_INVALID;
     if (q_type != MLA_FA_F16 && q_type != MLA_FA_BF16) return MLA_FA_ERR_INVALID;
     if (kv_type != MLA_FA_F16 && kv_type != MLA_FA_BF16 && kv_type != MLA_FA_Q8_0) return MLA_FA_ERR_INVALID;
@@ -403,7 +444,9 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
     a.n_head = n_head;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
-    hipError_t e = launch_mha(a, kv_kind_of(kv_type), static_cast<hipStream_t>(stream));
+    bool fail;
+    hipError_t e = launch_skipped(&fail) ? skipped_status(fail)
+                                         : launch_mha(a, kv_kind_of(kv_type), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -418,6 +461,7 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
                     int n_tok, int n_head, int64_t n_kv, const int32_t *kv_len, int causal, const uint16_t *mask,
                     int64_t mask_seq_stride, int64_t mask_tok_stride, float scale, float *out, int n_split,
                     void *workspace, size_t workspace_bytes, void *stream) {
+    begin_call();
     if (!q_nope || !q_pe || !w_uk || !w_uv || !out) return MLA_FA_ERR_INVALID;
     if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
         !aligned(out, 16) || !aligned(workspace, 256))
@@ -457,7 +501,7 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
     qa.c = ws + lay.q_off; qa.c_rs = (int64_t)n_head * kDK; qa.c_hs = kDK;
     qa.extra = static_cast<const uint16_t *>(q_pe); qa.extra_rs = (int64_t)n_head * 64; qa.extra_hs = 64;
     qa.M = (int)n_rows; qa.N = kDV; qa.K = 128; qa.H = n_head;
-    if (launch_proj(qa, kind, false, false, s) != hipSuccess) return MLA_FA_ERR_HIP;
+    if (run_proj(qa, kind, false, false, s) != hipSuccess) return MLA_FA_ERR_HIP;
     st = run_partials(c, p, s);
     if (st) return st;
     st = run_merge(n_rows, n_head, p.n_split, c.out, c.ws, c.ws_bytes, s);
@@ -468,18 +512,21 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
     oa.c = out; oa.c_rs = (int64_t)n_head * 128; oa.c_hs = 128;
     oa.extra = nullptr; oa.extra_rs = 0; oa.extra_hs = 0;
     oa.M = (int)n_rows; oa.N = 128; oa.K = kDV; oa.H = n_head;
-    return launch_proj(oa, kind, true, true, s) == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+    return run_proj(oa, kind, true, true, s) == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
 int fa_mask_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                     int32_t *idx, int64_t idx_row_stride, int32_t *count, void *stream) {
+    begin_call();
     if (!mask || !idx || !count || n_rows < 1 || n_kv < 1 || n_kv > 0x7FFFFFFFLL)
         return MLA_FA_ERR_INVALID;
     if (!aligned(mask, 2) || !aligned(idx, 4) || !aligned(count, 4)) return MLA_FA_ERR_INVALID;
     if (idx_row_stride < n_kv || (n_rows > 1 && mask_row_stride < n_kv) || mask_row_stride < 0)
         return MLA_FA_ERR_INVALID;
-    hipError_t e = launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
-                                  static_cast<hipStream_t>(stream));
+    bool fail;
+    hipError_t e = launch_skipped(&fail) ? skipped_status(fail)
+                                         : launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride,
+                                                          count, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -491,6 +538,7 @@ size_t fa_mask_compact_workspace_size(int n_rows, int64_t n_kv) {
 int fa_mask_compact_ws(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                        int32_t *idx, int64_t idx_row_stride, int32_t *count, void *workspace,
                        size_t workspace_bytes, void *stream) {
+    begin_call();
     if (!mask || !idx || !count || n_rows < 1 || n_kv < 1 || n_kv > 0x7FFFFFFFLL)
         return MLA_FA_ERR_INVALID;
     if (!aligned(mask, 2) || !aligned(idx, 4) || !aligned(count, 4)) return MLA_FA_ERR_INVALID;
@@ -499,13 +547,17 @@ int fa_mask_compact_ws(const uint16_t *mask, int64_t mask_row_stride, int n_rows
     const size_t need = fa_mask_compact_workspace_size(n_rows, n_kv);
     const bool vec_rows = aligned(mask, 16) && (n_rows == 1 || mask_row_stride % 8 == 0);
     hipError_t e;
+    bool fail;
     if (need == 0 || !vec_rows) {     // the one-workgroup-per-row kernel; workspace untouched
-        e = launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
-                           static_cast<hipStream_t>(stream));
+        e = launch_skipped(&fail) ? skipped_status(fail)
+                                  : launch_compact(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
+                                                   static_cast<hipStream_t>(stream));
     } else {
         if (!workspace || workspace_bytes < need || !aligned(workspace, 4)) return MLA_FA_ERR_WORKSPACE;
-        e = launch_compact_chunked(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride, count,
-                                   static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
+        e = launch_skipped(&fail) ? skipped_status(fail)
+                                  : launch_compact_chunked(mask, mask_row_stride, n_rows, n_kv, idx, idx_row_stride,
+                                                           count, static_cast<int32_t *>(workspace),
+                                                           static_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }

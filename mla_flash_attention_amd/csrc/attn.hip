@@ -122,10 +122,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     const uint16_t *mrow = a.mask ? a.mask + (int64_t)s_idx * a.mask_seq_stride +
                                         (int64_t)t_idx * a.mask_tok_stride
                                   : nullptr;
-    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride : nullptr;
+    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride + (int64_t)t_idx * a.idx_tok_stride
+                              : nullptr;
     int64_t kend, chunk = a.split_chunk;
     if constexpr (IDX) {
-        const int64_t c = a.kv_idx_count[s_idx];
+        const int64_t c = a.kv_idx_count[row];          // one count per (sequence, token) row
         kend = c < 0 ? 0 : (c > a.n_kv ? a.n_kv : c);
         chunk = (kend + a.n_split - 1) / a.n_split;
         chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
@@ -160,10 +161,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     auto q_fix = [&](u32x4 v, bool ok) __attribute__((always_inline)) {
         if (!ok) v = u32x4{0, 0, 0, 0};
         if constexpr (kQ8) {
-            if (a.q_bf16) {   // bf16 -> f16 for the f16 MFMA
+            if (a.q_bf16) {   // bf16 -> f16 for the f16 MFMA, saturated to the f16 range
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[e] = pack_f16x2(bf16_bits_to_f32(v[e] & 0xFFFFu), bf16_bits_to_f32(v[e] >> 16));
+                    v[e] = pack_f16x2(sat_f16(bf16_bits_to_f32(v[e] & 0xFFFFu)), sat_f16(bf16_bits_to_f32(v[e] >> 16)));
             }
         }
         return v;
@@ -437,6 +438,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         // A code c becomes u = c + 128 (flip the sign bit); one v_perm builds the f16 pair
         // (1024 + u0, 1024 + u1), and (x - 1152) * d in packed f16 gives (c0 d, c1 d): the
         // subtraction is exact and the product is rounded once, as code * d to f16 is.
+        // |code * d| <= 128 * 511.75 = 65504 whenever |d| < 512, so only blocks with a
+        // larger scale can leave the f16 range; those (rare) lanes saturate their values
+        // to +-65504 instead of becoming infinite.
 #pragma clang fp contract(off)
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
         const unsigned *rw = reinterpret_cast<const unsigned *>(raw);
@@ -451,6 +455,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
             const unsigned dbits = odd ? (w[0] >> 16) : (w[0] & 0xFFFFu);
             const h2 dd = __builtin_bit_cast(h2, dbits | (dbits << 16));
             const h2 off = h2{(_Float16)1152.f, (_Float16)1152.f};
+            const bool big = (dbits & 0x7FFFu) >= 0x6000u;            // |d| >= 512 (or inf/NaN)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {                                // 8 values -> 16 B chunk
                 unsigned pk[4];
@@ -461,8 +466,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
                     const unsigned u = code ^ 0x80808080u;               // code + 128 per byte
                     const h2 x01 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00050004u));
                     const h2 x23 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(u, 0x64646464u, 0x00070006u));
-                    pk[2 * h] = __builtin_bit_cast(unsigned, (h2)((x01 - off) * dd));
-                    pk[2 * h + 1] = __builtin_bit_cast(unsigned, (h2)((x23 - off) * dd));
+                    h2 v01 = (x01 - off) * dd, v23 = (x23 - off) * dd;
+                    if (big) {
+                        v01 = sat_f16x2(v01);
+                        v23 = sat_f16x2(v23);
+                    }
+                    pk[2 * h] = __builtin_bit_cast(unsigned, v01);
+                    pk[2 * h + 1] = __builtin_bit_cast(unsigned, v23);
                 }
                 const int lc = 4 * b + c;                                // 16-byte chunk of the row
                 unsigned char *dp = lc < 64 ? f16tile + r * kVRow + 16 * lc
@@ -846,10 +856,11 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
     const uint16_t *mrow = a.mask ? a.mask + (int64_t)s_idx * a.mask_seq_stride +
                                         (int64_t)t_idx * a.mask_tok_stride
                                   : nullptr;
-    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride : nullptr;
+    const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride + (int64_t)t_idx * a.idx_tok_stride
+                              : nullptr;
     int64_t kend, chunk = a.split_chunk;
     if constexpr (IDX) {
-        const int64_t c = a.kv_idx_count[s_idx];
+        const int64_t c = a.kv_idx_count[row];          // one count per (sequence, token) row
         kend = c < 0 ? 0 : (c > a.n_kv ? a.n_kv : c);
         chunk = (kend + a.n_split - 1) / a.n_split;
         chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;

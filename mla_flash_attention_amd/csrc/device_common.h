@@ -47,6 +47,14 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
+// Clamp to the finite f16 range [-65504, 65504]: a value past it then converts to the
+// largest finite f16 instead of to infinity (NaN inputs are not defined for the path).
+__device__ __forceinline__ float sat_f16(float x) { return __builtin_fminf(__builtin_fmaxf(x, -65504.f), 65504.f); }
+__device__ __forceinline__ f16x2v sat_f16x2(f16x2v x) {
+    const f16x2v hi = {(_Float16)65504.f, (_Float16)65504.f};
+    return __builtin_elementwise_max(__builtin_elementwise_min(x, hi), -hi);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(unsigned short b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }

@@ -28,9 +28,10 @@ struct AttnArgs {
     const uint16_t *mask;          // f16 bits or nullptr
     int64_t mask_seq_stride;       // elements
     int64_t mask_tok_stride;       // elements
-    const int32_t *kv_idx;         // sparse index lists or nullptr
-    const int32_t *kv_idx_count;
-    int64_t idx_seq_stride;
+    const int32_t *kv_idx;         // sparse index lists or nullptr: row (s, t) at
+    const int32_t *kv_idx_count;   //   kv_idx + s * idx_seq_stride + t * idx_tok_stride,
+    int64_t idx_seq_stride;        //   its length at kv_idx_count[s * n_tok + t]
+    int64_t idx_tok_stride;
     float *out;                    // [n_seq*n_tok][n_head][512], used when n_split == 1
     float *ws;                     // partials, used when n_split > 1
     int64_t n_kv;
@@ -52,12 +53,12 @@ struct AttnArgs {
 };
 constexpr int kMaxGridY = 65535;   // rows per launch (the grid's y extent)
 
-// Partial layout inside the workspace, for R = n_seq*n_tok rows, H heads, S splits:
-//   m [S][R][H] fp32 (log2 domain), l [S][R][H] fp32, o [S][R][H][512] fp32.
-// Split partials, per (split, row, head): m and l (fp32), two fp32 scales, and the
-// unnormalised O as 512 f16 values, each 256-column half stored times 2^(15 - e) where
-// max |O| < 2^e over the half (the scale kept is 2^(e - 15)).  Every value keeps f16's
-// relative precision (2^-11) whatever the magnitude of the cache's values.
+// Split partials inside the workspace, for R = n_seq*n_tok rows, H heads, S splits, in
+// this order: m [S][R][H] fp32 (log2 units), l [S][R][H] fp32, scale [S][R][H][2] fp32,
+// O [S][R][H][512] f16.  O is the unnormalised output, each 256-column half stored times
+// 2^(15 - e) where max |O| < 2^e over the half (the scale kept is 2^(e - 15)), so every
+// value keeps f16's relative precision (2^-11) whatever the magnitude of the cache's
+// values.
 inline size_t partial_bytes(int64_t rows, int heads, int splits) {
     return (size_t)splits * rows * heads * (4 * sizeof(float) + kDV * sizeof(uint16_t));
 }

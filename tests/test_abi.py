@@ -175,13 +175,14 @@ def test_merge_validation(L):
 
 def _attend(L, **kw):
     a = dict(q=FAKE, qt=B.MLA_FA_BF16, kv=FAKE, kvt=B.MLA_FA_BF16, rs=1152, ss=1152 * 64, n_seq=2, n_tok=2,
-             H=128, n_kv=64, kv_len=None, causal=0, mask=None, ms=0, mt=0, alibi=None, sinks=None,
-             softcap=0.0, scale=0.1, out=FAKE, n_split=1, ws=None, wsb=0)
+             H=128, n_kv=64, kv_len=None, causal=0, mask=None, ms=0, mt=0, idx=None, cnt=None, iss=0, its=0,
+             alibi=None, sinks=None, softcap=0.0, scale=0.1, out=FAKE, n_split=1, ws=None, wsb=0)
     a.update(kw)
     return L.mla_fa_attend(a["q"], a["qt"], a["kv"], a["kvt"], a["rs"], a["ss"], a["n_seq"], a["n_tok"],
                            a["H"], a["n_kv"], a["kv_len"], a["causal"], a["mask"], a["ms"], a["mt"],
-                           a["alibi"], a["sinks"], ctypes.c_float(a["softcap"]), ctypes.c_float(a["scale"]),
-                           a["out"], a["n_split"], a["ws"], a["wsb"], None)
+                           a["idx"], a["cnt"], a["iss"], a["its"], a["alibi"], a["sinks"],
+                           ctypes.c_float(a["softcap"]), ctypes.c_float(a["scale"]), a["out"], a["n_split"],
+                           a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -195,6 +196,14 @@ def _attend(L, **kw):
     (dict(H=120), B.MLA_FA_ERR_UNSUPPORTED),                         # heads not a multiple of 16
     (dict(qt=B.MLA_FA_F16, kvt=B.MLA_FA_BF16), B.MLA_FA_ERR_UNSUPPORTED),
     (dict(n_split=4, ws=FAKE, wsb=16), B.MLA_FA_ERR_WORKSPACE),      # workspace too small
+    (dict(idx=FAKE), B.MLA_FA_ERR_INVALID),                          # index lists without counts
+    (dict(cnt=FAKE), B.MLA_FA_ERR_INVALID),                          # counts without index lists
+    (dict(idx=FAKE, cnt=FAKE, iss=128, its=64, causal=1), B.MLA_FA_ERR_INVALID),   # sparse + causal
+    (dict(idx=FAKE, cnt=FAKE, iss=128, its=64, kv_len=FAKE), B.MLA_FA_ERR_INVALID),  # sparse + lengths
+    (dict(idx=FAKE + 2, cnt=FAKE, iss=128, its=64), B.MLA_FA_ERR_INVALID),  # misaligned lists
+    (dict(idx=FAKE, cnt=FAKE, iss=128, its=63), B.MLA_FA_ERR_INVALID),     # token rows overlap
+    (dict(idx=FAKE, cnt=FAKE, iss=63, its=64), B.MLA_FA_ERR_INVALID),      # sequence rows overlap
+    (dict(idx=FAKE, cnt=FAKE, iss=-128, its=64), B.MLA_FA_ERR_INVALID),
 ])
 def test_attend_validation(L, kw, status):
     assert _attend(L, **kw) == status
@@ -264,3 +273,38 @@ def test_absorbed_workspace_size(L):
     assert n >= 4 * 128 * (576 * 2 + 512 * 4)
     assert L.mla_fa_absorbed_workspace_size(4, 128, 32768, B.MLA_FA_BF16, 8) > n    # plus the partials
     assert L.mla_fa_absorbed_workspace_size(0, 128, 32768, B.MLA_FA_BF16, 1) == 0
+
+
+# ---------------------------------------------------------------- launch failures
+# MLA_FA_FAIL_LAUNCH=k: the call launches nothing and reports its k-th launch as failed,
+# so every MLA_FA_ERR_HIP return is reached here without a GPU.
+@pytest.mark.parametrize("k,status", [(1, B.MLA_FA_ERR_HIP), (2, B.MLA_FA_ERR_HIP), (3, B.MLA_FA_OK)])
+def test_decode_launch_failure(L, monkeypatch, k, status):
+    """Decode with splits is two launches: the attention, then the merge."""
+    monkeypatch.setenv("MLA_FA_FAIL_LAUNCH", str(k))
+    assert _decode(L, n_split=4, ws=FAKE, wsb=1 << 30) == status
+    assert _decode(L, n_split=1) == (B.MLA_FA_ERR_HIP if k == 1 else B.MLA_FA_OK)   # one launch
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_two_phase_and_prefill_launch_failures(L, monkeypatch, k):
+    monkeypatch.setenv("MLA_FA_FAIL_LAUNCH", str(k))
+    exp = B.MLA_FA_ERR_HIP if k == 1 else B.MLA_FA_OK
+    assert L.mla_fa_decode_partials(FAKE, B.MLA_FA_BF16, FAKE, B.MLA_FA_BF16, 1152, 1152 * 64, 1, 128, 64, None, 0,
+                                    None, None, 0, ctypes.c_float(0.1), FAKE, 4, FAKE, 1 << 30, None) == exp
+    assert L.mla_fa_merge_partials(4, 128, 8, FAKE, FAKE, 1 << 30, None) == exp
+    pre = L.mla_fa_prefill(FAKE, B.MLA_FA_BF16, FAKE, B.MLA_FA_BF16, 1152, 8, 128, 16, 1, None, 0,
+                           ctypes.c_float(0.1), FAKE, 2, FAKE, 1 << 30, None)
+    assert pre == B.MLA_FA_ERR_HIP
+    assert _attend(L, n_split=2, ws=FAKE, wsb=1 << 30) == B.MLA_FA_ERR_HIP
+    assert _mha(L) == exp
+    assert L.fa_mask_compact(FAKE, 100, 1, 100, FAKE, 100, FAKE, None) == exp
+    assert L.fa_mask_compact_ws(FAKE, 4096, 1, 4096, FAKE, 4096, FAKE, FAKE, 1 << 20, None) == exp   # chunked
+    assert L.fa_mask_compact_ws(FAKE + 2, 100, 1, 100, FAKE, 100, FAKE, None, 0, None) == exp        # one-WG (unaligned)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_absorbed_launch_failures(L, monkeypatch, k):
+    """Absorbed decode with splits: query projection, attention, merge, output projection."""
+    monkeypatch.setenv("MLA_FA_FAIL_LAUNCH", str(k))
+    assert _absorbed(L, n_split=4) == (B.MLA_FA_ERR_HIP if k <= 4 else B.MLA_FA_OK)

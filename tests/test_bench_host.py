@@ -61,7 +61,7 @@ def test_counter_files_to_bytes_per_launch(tmp_path, monkeypatch):
     (tmp_path / "profiles").mkdir()
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "_source_hash", lambda: "feedfacefeedface")
-    bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    bench.write_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "decode_c2")
     d = json.loads((tmp_path / "profiles" / "hbm_traffic.json").read_text())["decode_c2"]
     assert d["source_hash"] == "feedfacefeedface"
     assert d["counters"]["FETCH_SIZE"]["kib_per_launch"] == 100.0

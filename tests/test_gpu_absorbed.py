@@ -61,11 +61,9 @@ def test_absorbed_repeat_is_bitwise_stable():
     assert np.array_equal(run_absorbed(p, 2), run_absorbed(p, 2))
 
 
-def test_absorbed_full_size_decode_sampled():
+def test_absorbed_full_size_decode():
     """4 sequences x 128 heads over 32768-cell caches (the decode workload's shape), the
-    benched launch; rows sampled across sequences and heads."""
+    benched launch: every output row against the oracle."""
     p = synth.make_absorbed_problem(4, 1, 128, 32768, BF16, BF16, seed=9)
     got = run_absorbed(p)
-    assert np.all(np.isfinite(got))
-    rows = np.array([0, 1, 63, 64, 127, 128, 200, 255, 256, 300, 383, 384, 450, 511])
-    assert_parity(got[rows], ref_absorbed(p, rows=rows), "absorbed 4x128h n_kv=32768 sampled")
+    assert_parity(got, ref_absorbed(p), "absorbed 4x128h n_kv=32768")

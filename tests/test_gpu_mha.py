@@ -113,15 +113,10 @@ def test_mha_repeat_is_bitwise_stable():
     assert np.array_equal(a, b)
 
 
-def test_mha_full_size_sampled():
-    """2048 tokens x 128 heads over a 4096-key cache (causal), the benched launch; rows
-    sampled across token tiles, tile edges and heads, checked against the oracle."""
+def test_mha_full_size():
+    """2048 tokens x 128 heads over a 4096-key cache (causal), the benched launch: every
+    output row against the oracle."""
     n_tok, n_head, n_kv = 2048, 128, 4096
     p = synth.make_mha_problem(n_tok, n_head, n_kv, BF16, BF16, seed=16, causal=True)
     got = run_mha(p)
-    assert np.all(np.isfinite(got))
-    g = np.random.default_rng(16)
-    toks = np.concatenate([[0, 1, 255, 256, 511, 1023, 1024, 2046, 2047], g.integers(0, n_tok, 40)])
-    heads = np.concatenate([[0, 127], g.integers(0, n_head, len(toks) - 2)])
-    rows = toks * n_head + heads
-    assert_parity(got[rows], ref_mha(p, rows=rows), "mha 2048x128 n_kv=4096 sampled")
+    assert_parity(got, ref_mha(p), "mha 2048x128 n_kv=4096")

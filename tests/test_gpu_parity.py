@@ -63,15 +63,12 @@ def test_c5_full_sparse(chunked):
     assert_parity(got, oracle.attention_problem(p), "C5")
 
 
-def test_c3_full_sampled_rows():
-    """Full prefill; rows checked: first/last tokens, tile edges, random tokens."""
+def test_c3_full():
+    """The full causal prefill (2048 tokens x 128 heads over 4096 cells, the benched launch):
+    every output row against the oracle."""
     p = synth.make_config(3)
     got = run_prefill(p)
-    toks = sorted({0, 1, 63, 64, 65, 1023, 1024, 2046, 2047} |
-                  set(np.random.default_rng(0).integers(0, 2048, 8).tolist()))
-    rows = np.array([t * 128 + h for t in toks for h in range(128)])
-    ref = oracle.attention_problem(p, rows=rows)
-    assert_parity(got[rows], ref, "C3 sampled tokens")
+    assert_parity(got, oracle.attention_problem(p), "C3")
 
 
 # ---------------------------------------------------------------- reduced-size sweeps
