@@ -150,6 +150,29 @@ int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const
                           size_t workspace_bytes, void *stream);
 
 /*
+ * mla_fa_decode for callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, arguments and errors as mla_fa_decode, without the workspace.  The split
+ * partials live in a library-owned scratch array of MLA_FA_NOALLOC_SCRATCH_BYTES in
+ * device memory, one per GPU, held until the process ends; the call allocates nothing.
+ * It uses the scratch of the current device, which must be the device of `stream`.
+ *   - The automatic split count (n_split = 0, no MLA_FA_NSPLIT override) always fits:
+ *     its partials never exceed 33,945,600 bytes (255 rows of 64 heads at 2 splits).
+ *     A call whose partials (mla_fa_workspace_size with the same sizes) exceed the
+ *     scratch returns MLA_FA_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on one GPU shares that GPU's scratch and fully rewrites what it reads,
+ *     so nothing needs clearing; calls that overlap on one GPU (other streams, other
+ *     threads) race on it and must be serialised by the caller.
+ *   - The first call on each device looks up the scratch's device address (no
+ *     allocation); a failure there returns MLA_FA_ERR_HIP.
+ */
+#define MLA_FA_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20)
+int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                          int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv, const uint16_t *mask,
+                          int64_t mask_seq_stride, const int32_t *kv_idx, const int32_t *kv_idx_count,
+                          int64_t idx_seq_stride, float scale, float *out, int n_split, void *stream);
+
+/*
  * Chunked prefill: n_tok query tokens of one sequence against its cache of n_kv rows
  * (the chunk's tokens are the last n_tok positions of the cache).
  *   q        [n_tok][n_head][576] f16/bf16 bits.

@@ -21,7 +21,8 @@ MLA_FA_F16, MLA_FA_BF16, MLA_FA_Q8_0 = synth.TYPE_F16, synth.TYPE_BF16, synth.TY
 MLA_FA_OK, MLA_FA_ERR_INVALID, MLA_FA_ERR_UNSUPPORTED, MLA_FA_ERR_WORKSPACE, MLA_FA_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("mla_fa_strerror", "mla_fa_version", "mla_fa_auto_splits", "mla_fa_workspace_size",
-           "mla_fa_decode", "mla_fa_decode_partials", "mla_fa_merge_partials", "mla_fa_prefill",
+           "mla_fa_decode", "mla_fa_decode_noalloc", "mla_fa_decode_partials", "mla_fa_merge_partials",
+           "mla_fa_prefill",
            "mla_fa_attend", "mla_fa_prefill_mha", "mla_fa_absorbed_workspace_size", "mla_fa_absorbed",
            "fa_mask_compact", "fa_mask_compact_workspace_size", "fa_mask_compact_ws")
 
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         dec = [_p, _i, _p, _i, _i64, _i64, _i, _i, _i64, _p, _i64, _p, _p, _i64, _f, _p, _i, _p, _sz, _p]
         L.mla_fa_decode.restype = _i
         L.mla_fa_decode.argtypes = dec
+        L.mla_fa_decode_noalloc.restype = _i
+        L.mla_fa_decode_noalloc.argtypes = dec[:-3] + [_p]
         L.mla_fa_decode_partials.restype = _i
         L.mla_fa_decode_partials.argtypes = dec
         L.mla_fa_merge_partials.restype = _i
@@ -145,6 +148,15 @@ def mla_fa_decode(q, q_type, kv, kv_type, scale, out, *, mask=None, kv_idx=None,
     _check(lib().mla_fa_decode(*_decode_args(q, q_type, kv, kv_type, scale, out, mask, kv_idx,
                                              kv_idx_count, n_split, workspace, stream)),
            "mla_fa_decode")
+    return out
+
+
+def mla_fa_decode_noalloc(q, q_type, kv, kv_type, scale, out, *, mask=None, kv_idx=None, kv_idx_count=None,
+                          n_split=0, stream=None):
+    """mla_fa_decode without a workspace: the split partials live in the library's
+    per-GPU scratch (include/mla_fa.h); same arguments otherwise."""
+    a = _decode_args(q, q_type, kv, kv_type, scale, out, mask, kv_idx, kv_idx_count, n_split, None, stream)
+    _check(lib().mla_fa_decode_noalloc(*(a[:-3] + (a[-1],))), "mla_fa_decode_noalloc")
     return out
 
 

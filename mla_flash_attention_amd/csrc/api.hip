@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mla_fa.h"
 #include "mla_fa_internal.h"
@@ -281,6 +282,31 @@ AbsorbedLayout absorbed_layout(int64_t n_rows, int n_head, int n_split) {
     return l;
 }
 
+// Scratch of mla_fa_decode_noalloc: the split partials of callers that cannot allocate.
+// Each GPU the library runs on holds its own copy for the life of the process.  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = MLA_FA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (nullptr on a HIP error).
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,6 +380,30 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
     st = run_partials(c, p, s);
     if (st) return st;
     return run_merge(n_seq, n_head, p.n_split, out, workspace, workspace_bytes, s);
+}
+
+int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
+                          int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv, const uint16_t *mask,
+                          int64_t mask_seq_stride, const int32_t *kv_idx, const int32_t *kv_idx_count,
+                          int64_t idx_seq_stride, float scale, float *out, int n_split, void *stream) {
+    begin_call();
+    Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
+                             mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
+                             n_split, nullptr, 0);
+    int st = validate(c);
+    if (st) return st;
+    Plan p = make_plan(n_seq, n_head, n_kv, kv_type, n_split);
+    const size_t need = p.n_split > 1 ? partial_bytes(n_seq, n_head, p.n_split) : 0;
+    if (need > kScratchBytes) return MLA_FA_ERR_WORKSPACE;      // past the scratch's fixed size
+    if (need) {
+        c.ws = device_scratch();
+        if (!c.ws) return MLA_FA_ERR_HIP;
+        c.ws_bytes = kScratchBytes;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = run_partials(c, p, s);
+    if (st) return st;
+    return run_merge(n_seq, n_head, p.n_split, out, c.ws, c.ws_bytes, s);
 }
 
 int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
