@@ -157,7 +157,7 @@ int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const
  * device memory, one per GPU, held until the process ends; the call allocates nothing.
  * It uses the scratch of the current device, which must be the device of `stream`.
  *   - The automatic split count (n_split = 0, no MLA_FA_NSPLIT override) always fits:
- *     its partials never exceed 33,945,600 bytes (255 rows of 64 heads at 2 splits).
+ *     its partials never exceed 42,598,400 bytes (80 rows of 128 heads, Q8_0, 4 splits).
  *     A call whose partials (mla_fa_workspace_size with the same sizes) exceed the
  *     scratch returns MLA_FA_ERR_WORKSPACE and enqueues nothing.
  *   - Every call on one GPU shares that GPU's scratch and fully rewrites what it reads,
@@ -166,7 +166,7 @@ int mla_fa_merge_partials(int n_rows, int n_head, int n_split, float *out, const
  *   - The first call on each device looks up the scratch's device address (no
  *     allocation); a failure there returns MLA_FA_ERR_HIP.
  */
-#define MLA_FA_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20)
+#define MLA_FA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
                           int64_t kv_seq_stride, int n_seq, int n_head, int64_t n_kv, const uint16_t *mask,
                           int64_t mask_seq_stride, const int32_t *kv_idx, const int32_t *kv_idx_count,

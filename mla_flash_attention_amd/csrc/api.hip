@@ -68,11 +68,18 @@ int env_splits() {
     return v >= 1 && v <= kMaxSplits ? v : 0;
 }
 
-// Workgroup shape: heads per workgroup.  Split calls use 64-head workgroups whose two
-// key halves merge in LDS (half the partial bytes of 128-head workgroups); unsplit calls
-// use 128-head workgroups so each tile is read once per query row.  The pair-kernel
-// shapes (p64, p128: half the LDS reads per MFMA, two exchanges per stage) are selected
-// only through the tuning override; measured on gfx950 they do not beat these.
+// Workgroup shape: heads per workgroup.  Split calls over 16-bit caches use 64-head
+// workgroups whose two key halves merge in LDS (half the partial bytes of 128-head
+// workgroups); unsplit calls use 128-head workgroups so each tile is read once per query
+// row.  Q8_0 caches use 128-head workgroups while that takes at most 64 splits: each
+// dequantised tile then serves every head (measured on the 4 x 128-head x 65536-cell
+// Q8_0 decode: kernel 116 -> 97 us with twice the splits); past that (one or two rows,
+// as in sparse decoding) twice the partials cost more than the dequantisation saves
+// (the 131,072-cell sparse Q8_0 step: 40 -> 52 us).  The pair-kernel shapes (p64, p128: half the LDS reads per
+// MFMA, two exchanges per stage) are selected only through the tuning override; measured
+// on gfx950 they do not beat these.
+constexpr int kQ8WideMaxSplits = 64;
+
 int pick_shape(int n_head, int n_split, int kv_type) {
     if (const char *e = std::getenv("MLA_FA_SHAPE")) {       // tuning only
         const bool q8 = kv_type == MLA_FA_Q8_0;
@@ -85,18 +92,27 @@ int pick_shape(int n_head, int n_split, int kv_type) {
     }
     if (n_head <= 16) return SHAPE_H16;
     if (n_head <= 32) return SHAPE_H32;
-    if (n_head <= 64 || n_split > 1) return SHAPE_H64;
-    return SHAPE_H128;
+    if (n_head <= 64) return SHAPE_H64;
+    if (n_split <= 1) return SHAPE_H128;
+    return kv_type == MLA_FA_Q8_0 && n_split <= kQ8WideMaxSplits ? SHAPE_H128 : SHAPE_H64;
 }
 
 int auto_splits(int64_t n_rows, int n_head, int64_t n_kv, int kv_type) {
     const int env = env_splits();
     if (env) return env;
-    const int hs = shape_heads(pick_shape(n_head, 2, kv_type));
     const int hu = shape_heads(pick_shape(n_head, 1, kv_type));
-    const int hg_split = (n_head + hs - 1) / hs;
     if (n_rows * ((n_head + hu - 1) / hu) >= kCUs) return 1;
-    int64_t s = (kCUs + n_rows * hg_split - 1) / (n_rows * hg_split);
+    // splits that fill the chip with the split shape: the wide Q8_0 shape when that plan
+    // stays within its split limit, else the 16-bit one
+    int hs = shape_heads(pick_shape(n_head, 2, kv_type));
+    int64_t s = (kCUs + n_rows * ((n_head + hs - 1) / hs) - 1) / (n_rows * ((n_head + hs - 1) / hs));
+    // (the wide shape also needs the rounded-up plan to stay near one workgroup per CU)
+    if (shape_heads(pick_shape(n_head, (int)(s < kMaxSplits ? s : kMaxSplits), kv_type)) != hs ||
+        n_rows * s * ((n_head + hs - 1) / hs) > kCUs + kCUs / 4) {
+        hs = shape_heads(pick_shape(n_head, kMaxSplits, kv_type));
+        const int64_t hg = (n_head + hs - 1) / hs;
+        s = (kCUs + n_rows * hg - 1) / (n_rows * hg);
+    }
     const int64_t max_by_len = (n_kv + kTileKeys * kMinTilesPerSplit - 1) / (kTileKeys * kMinTilesPerSplit);
     if (s > max_by_len) s = max_by_len;
     if (s < 1) s = 1;

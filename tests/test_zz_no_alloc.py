@@ -14,7 +14,7 @@ from mla_flash_attention_amd import synth
 from tests.gpu_common import assert_parity, to_dev
 
 BF16, Q8 = synth.TYPE_BF16, synth.TYPE_Q8_0
-SCRATCH = 36 << 20          # MLA_FA_NOALLOC_SCRATCH_BYTES in include/mla_fa.h
+SCRATCH = 48 << 20          # MLA_FA_NOALLOC_SCRATCH_BYTES in include/mla_fa.h
 FAKE = 1 << 20
 
 
