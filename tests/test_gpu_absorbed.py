@@ -49,6 +49,10 @@ def ref_absorbed(p, rows=None):
     (dict(n_seq=2, n_tok=2, n_head=16, n_kv=400, q_type=BF16, kv_type=BF16, seed=5, mask_kind="runs_bias"), 2),
     (dict(n_seq=1, n_tok=200, n_head=16, n_kv=400, q_type=BF16, kv_type=BF16, seed=6, causal=True), 1),
     (dict(n_seq=1, n_tok=130, n_head=48, n_kv=260, q_type=F16, kv_type=F16, seed=7, causal=True), 0),
+    # 16 and 17 rows with splits (decode-sized batches), a Q8_0 cache at 128 heads
+    (dict(n_seq=8, n_tok=2, n_head=64, n_kv=900, q_type=BF16, kv_type=BF16, seed=10, causal=True), 3),
+    (dict(n_seq=17, n_tok=1, n_head=32, n_kv=700, q_type=F16, kv_type=F16, seed=11), 5),
+    (dict(n_seq=3, n_tok=1, n_head=128, n_kv=2000, q_type=BF16, kv_type=Q8, seed=12), 0),
 ])
 def test_absorbed(kw, n_split):
     p = synth.make_absorbed_problem(**kw)
