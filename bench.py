@@ -58,7 +58,7 @@ def _args():
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
                          "--copy-calibration into profiles/hbm_traffic.json and exit")
     ap.add_argument("--traffic-key", default="decode_c2",
-                    help="workload the --traffic-from runs timed (decode_c2, decode_c4_q8_0)")
+                    help="workload the --traffic-from runs timed (decode_c2, decode_c4_q8_0, sparse_c5)")
     return ap.parse_args()
 
 
@@ -73,31 +73,42 @@ def _counter_rows(d):
 
 
 def write_traffic(fetch_dir, write_dir, key):
-    """HBM bytes per launch of the split-attention kernel from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by what the same counter reads for a 1 GiB device
-    copy (copy reads 1 GiB and writes 1 GiB); stored under `key` (the workload the two
-    counter runs timed) in profiles/hbm_traffic.json."""
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for a 1 GiB device copy (copy reads 1 GiB and writes
+    1 GiB); stored under `key` (the workload the two counter runs timed) in
+    profiles/hbm_traffic.json: per kernel name (medians over its dispatches), and at the
+    top level for the attention kernel when the runs launched exactly one."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     out = {}
     if os.path.exists(path):
         with open(path) as f:
             out = json.load(f)
-    per = {}
+    per, kernels = {}, {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == name]
-        attn = [float(r["Counter_Value"]) for r in rows if "attn_kernel" in r["Kernel_Name"]]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower()]
+        is_copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+        copy = [float(r["Counter_Value"]) for r in rows if is_copy(r["Kernel_Name"])]
         copy = [c for c in copy if c > 1e5]          # the 1 GiB copy, not small fills
-        if not attn or not copy:
-            raise SystemExit(f"{name}: no attention or copy dispatches in {d}")
+        if not copy:
+            raise SystemExit(f"{name}: no calibration copy in {d}")
         factor = (1 << 30) / (max(copy) * 1024.0)    # bytes per counted KiB
-        per[name] = dict(kib_per_launch=float(np.median(attn)), copy_kib=max(copy), factor=factor,
-                         bytes_per_launch=float(np.median(attn)) * 1024.0 * factor)
-    out[key] = dict(source_hash=_source_hash(),
-                            bytes_per_launch=per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"],
-                            read_bytes=per["FETCH_SIZE"]["bytes_per_launch"],
-                            write_bytes=per["WRITE_SIZE"]["bytes_per_launch"], counters=per)
+        by_kernel = {}
+        for r in rows:
+            if not is_copy(r["Kernel_Name"]):
+                by_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        field = "read_bytes" if name == "FETCH_SIZE" else "write_bytes"
+        for kn, v in by_kernel.items():
+            kernels.setdefault(kn, {})[field] = float(np.median(v)) * 1024.0 * factor
+        attn = [kn for kn in by_kernel if "attn_kernel" in kn]
+        if len(attn) == 1:
+            kib = float(np.median(by_kernel[attn[0]]))
+            per[name] = dict(kib_per_launch=kib, copy_kib=max(copy), factor=factor, bytes_per_launch=kib * 1024.0 * factor)
+    entry = dict(source_hash=_source_hash(), kernels=kernels)
+    if len(per) == 2:
+        entry.update(bytes_per_launch=per["FETCH_SIZE"]["bytes_per_launch"] + per["WRITE_SIZE"]["bytes_per_launch"],
+                     read_bytes=per["FETCH_SIZE"]["bytes_per_launch"],
+                     write_bytes=per["WRITE_SIZE"]["bytes_per_launch"], counters=per)
+    out[key] = entry
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out[key], indent=1))
@@ -112,7 +123,7 @@ def _dev(a):
 def _source_hash():
     """Hash of the sources that decide the split-attention kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
+    for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
         with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -130,6 +141,18 @@ def _traffic(kernel_key):
     if not e or e.get("source_hash") != _source_hash():
         return None
     return e.get("bytes_per_launch")
+
+
+def _traffic_by_kernel(key):
+    """{kernel name: {read_bytes, write_bytes}} measured for workload `key`, or None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        e = json.load(f).get(key)
+    if not e or e.get("source_hash") != _source_hash():
+        return None
+    return e.get("kernels")
 
 
 WARM_FLOOR_S = 0.1   # minimum warm-up time before every timed loop
@@ -392,6 +415,21 @@ def _sparse_line(p, r):
     compact_bytes = 2 * p.n_kv * p.n_seq + 4 * cells + 4 * p.n_seq
     merge_bytes = partial_bytes + p.n_seq * p.n_head * 512 * 4
     frac = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    # HBM bytes per launch measured with rocprofv3 counters (profiles/hbm_traffic.json,
+    # the same seeded workload), when taken on the current kernel sources
+    traffic = None
+    t = _traffic_by_kernel("sparse_c5")
+    if t:
+        from mla_flash_attention_amd import synth
+        kind = {synth.TYPE_BF16: 0, synth.TYPE_F16: 1, synth.TYPE_Q8_0: 2}[p.kv_type]   # template argument
+
+        def measured(match):
+            m = [v for k, v in t.items() if match(k)]
+            return m[0].get("read_bytes", 0.0) + m[0].get("write_bytes", 0.0) if len(m) == 1 else None
+        cnt, wr = measured(lambda k: "chunk_count_kernel" in k), measured(lambda k: "chunk_write_kernel" in k)
+        traffic = {"compaction": cnt + wr if cnt is not None and wr is not None else None,
+                   "attention": measured(lambda k: "attn_kernel" in k and f", {kind}, true>" in k),
+                   "merge": measured(lambda k: "merge_kernel" in k)}
     return dict(ms=r["step_ms"], compact_ms=r["compact_ms"], compaction="fa_mask_compact_ws (4096-cell chunks)",
                 attn_ms=r["part_ms"], merge_ms=r["merge_ms"], kept=kept, n_split=ns,
                 kept_row_bytes=cells * ROW_BYTES[p.kv_type], partial_bytes=partial_bytes,
@@ -399,7 +437,9 @@ def _sparse_line(p, r):
                 kept_cells_per_s=kept / (r["step_ms"] * 1e-3),
                 hbm_frac={"compaction": frac(compact_bytes, r["compact_ms"]), "attention": frac(kb, r["part_ms"]),
                           "merge": frac(merge_bytes, r["merge_ms"]) if r["merge_ms"] else None,
-                          "step": frac(cb, r["step_ms"])})
+                          "step": frac(cb, r["step_ms"])},
+                algorithmic_bytes={"compaction": compact_bytes, "attention": kb, "merge": merge_bytes},
+                traffic=traffic)
 
 
 def _measured_peaks(torch, reps=5):
