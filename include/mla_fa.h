@@ -275,8 +275,9 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
  * local inference", sections 3.2-3.3 and 6.1).  For row r = (s, t) and head h:
  *     q_lat = W_UK[h] q_nope[r][h]                  (512; rounded to q_type on the GPU)
  *     O     = latent attention of [q_lat, q_pe[r][h]] as mla_fa_attend computes it
- *     out[r][h] = W_UV[h] O                         (128; O rounded to q_type as the
- *                                                    MFMA operand, fp32 accumulation)
+ *     out[r][h] = W_UV[h] O                         (128; O as a q_type head plus the
+ *                                                    q_type rounding of its remainder,
+ *                                                    two MFMA operands, fp32 accumulation)
  *   q_nope   [n_seq][n_tok][n_head][128], q_pe [n_seq][n_tok][n_head][64]: q_type bits
  *            (f16 or bf16), device, 16-byte aligned.
  *   w_uk     [n_head][512][128], w_uv [n_head][128][512]: q_type bits, stored
@@ -287,9 +288,11 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
  *   workspace  device, 256-byte aligned, at least mla_fa_absorbed_workspace_size(
  *            n_seq*n_tok, n_head, n_kv, kv_type, n_split) bytes: it holds the 576-wide
  *            queries, the latent outputs and the split partials.
- * Four launches on `stream`: query projection (with the q_pe copy), attention, merge
- * (when split), output projection.  Errors as for mla_fa_attend; ERR_WORKSPACE when the
- * workspace is missing or short.
+ * Three launches on `stream`: the query projection (with the q_pe copy), the attention,
+ * then the output projection, which for a split plan is fused with the merge of the
+ * split partials (the epilogue reads the partials and W_UV; the merged latent output
+ * never reaches memory).  Errors as for mla_fa_attend; ERR_WORKSPACE when the workspace
+ * is missing or short.
  */
 size_t mla_fa_absorbed_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split);
 int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void *w_uk, const void *w_uv,

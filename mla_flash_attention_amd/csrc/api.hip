@@ -570,8 +570,17 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
     if (run_proj(qa, kind, false, false, s) != hipSuccess) return MLA_FA_ERR_HIP;
     st = run_partials(c, p, s);
     if (st) return st;
-    st = run_merge(n_rows, n_head, p.n_split, c.out, c.ws, c.ws_bytes, s);
-    if (st) return st;
+    if (p.n_split > 1) {
+        // split plan: the merge and the output projection are one launch
+        MergeProjArgs ma;
+        ma.ws = static_cast<const float *>(c.ws);
+        ma.w = static_cast<const uint16_t *>(w_uv);
+        ma.out = out; ma.out_rs = (int64_t)n_head * 128;
+        ma.n_rows = (int)n_rows; ma.n_head = n_head; ma.n_split = p.n_split;
+        bool fail;
+        const hipError_t e = launch_skipped(&fail) ? skipped_status(fail) : launch_merge_proj(ma, kind, s);
+        return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
+    }
     ProjArgs oa;
     oa.a = c.out; oa.a_rs = (int64_t)n_head * kDV; oa.a_hs = kDV;
     oa.w = static_cast<const uint16_t *>(w_uv);

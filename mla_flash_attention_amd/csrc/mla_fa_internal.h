@@ -95,7 +95,20 @@ struct ProjArgs {
     int M, N, K, H;
 };
 
+// The merge of split partials fused with the output projection of absorbed attention:
+// out[r][h][n] = sum_k W[h][n][k] * O[r][h][k] for n < 128, k < 512, where O[r][h] is the
+// merged latent output (as merge_kernel computes it); W 16-bit [H][128][512], out fp32 at
+// out + r * out_rs + h * 128 + n.
+struct MergeProjArgs {
+    const float *ws;               // the split partials (layout of partial_bytes)
+    const uint16_t *w;
+    float *out;
+    int64_t out_rs;                // elements
+    int n_rows, n_head, n_split;
+};
+
 hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);
+hipError_t launch_merge_proj(const MergeProjArgs &a, int kind, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &p, int kind, bool a_f32, bool c_f32, hipStream_t stream);
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
                         const float *sinks, hipStream_t stream);

@@ -224,7 +224,195 @@ __global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Split merge + output projection in one launch (the epilogue of split absorbed
+// decode).  A workgroup takes 4 query rows of one head and 64 of the 128 output
+// columns: it starts its share of W (64 x 512, 64 KiB) loading, merges the 4 rows'
+// partials into fp32 O in LDS (the merge rule of the plain path: weights 2^(m_i - m*),
+// empty splits weigh 0, per-half scales of the f16 values), then computes
+// C[n][r] = W[n] . O[r] on MFMA with the rows as the B operand's columns (4 of 16 used),
+// O split into a 16-bit head and remainder as in the separate projection.  The two
+// column halves of a (row block, head) are workgroups x and x + 8, so that they run on
+// one XCD and can share the partials through its L2.  (One workgroup per (row block,
+// head) over all 128 columns reads the partials once but runs on half the CUs: 12.0
+// against 10.2 us on the 4 x 128-head decode.)
+constexpr int kMPRows = 4;                      // query rows per workgroup
+constexpr int kMPThreads = 512;
+constexpr int kMPBatch = 16;                    // partial loads in flight per thread
+constexpr int kMPPer = kMaxSplits / 128;        // splits per factor thread
+
+template <int KIND>
+__global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a) {
+    __shared__ float fac_s[2][kMPRows][kMaxSplits];   // per-half factors: weight x scale
+    __shared__ float red_m[kMPThreads / 64], red_l[kMPThreads / 64];
+    __shared__ f32x4 part_s[kMPThreads];               // split group 1's sums
+    __shared__ __attribute__((aligned(16))) float o_s[kMPRows][kDV];
+    __shared__ f32x4 acc_s[4][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int wg = blockIdx.x;
+    const int half = (wg >> 3) & 1;                    // output columns 64 half .. + 63
+    const int rest = (wg >> 4) * 8 + (wg & 7);         // (row block, head)
+    const int n_rb = (a.n_rows + kMPRows - 1) / kMPRows;
+    if (rest >= n_rb * a.n_head) return;
+    const int h = rest % a.n_head, r0 = (rest / a.n_head) * kMPRows;
+    const int nrow = a.n_rows - r0 < kMPRows ? a.n_rows - r0 : kMPRows;
+    const int S = a.n_split;
+    const int64_t RH = (int64_t)a.n_rows * a.n_head;
+    const float *wm = a.ws;
+    const float *wl = wm + (int64_t)S * RH;
+    const f32x2v *wsc = reinterpret_cast<const f32x2v *>(wl + (int64_t)S * RH);
+    const uint16_t *wo = reinterpret_cast<const uint16_t *>(wsc + (int64_t)S * RH);
+
+    // W rows of this wave: n-block nb of the half, reduction half kh (8 steps of 32)
+    const int nb = wave & 3, kh = wave >> 2;
+    const uint16_t *wp = a.w + ((int64_t)h * 128 + 64 * half + 16 * nb + l16) * kDV + 256 * kh + 8 * g;
+    u32x4 wv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wv[s] = *reinterpret_cast<const u32x4 *>(wp + 32 * s);
+
+    // partial O loads of this thread: (row pr, octet oc) of the block, splits sg, sg + 2, ...
+    const int pair = tid & 255, sg = tid >> 8;
+    const int pr = pair >> 6, oc = pair & 63;
+    const bool prow = pr < nrow;
+    const u32x4 *op = reinterpret_cast<const u32x4 *>(wo + ((int64_t)(r0 + (prow ? pr : 0)) * a.n_head + h) * kDV) + oc;
+    const int64_t step8 = RH * kDV / 8;               // stride between splits, in octets
+    u32x4 v0[kMPBatch];
+#pragma unroll
+    for (int u = 0; u < kMPBatch; ++u) {
+        const int i = sg + 2 * u;
+        v0[u] = op[(int64_t)(i < S ? i : 0) * step8];   // unconditional: no wait until used
+    }
+
+    // (m, l, scales) of row fr, splits ft, ft + 128, ...: max, weights, normaliser
+    const int fr = tid >> 7, ft = tid & 127;
+    const bool frow = fr < nrow;
+    const int64_t rhf = (int64_t)(r0 + (frow ? fr : 0)) * a.n_head + h;
+    float mv[kMPPer], lv[kMPPer];
+    f32x2v scv[kMPPer];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMPPer; ++j) {
+        const int i = ft + 128 * j;
+        mv[j] = -INFINITY;
+        if (frow && i < S) {
+            mv[j] = wm[i * RH + rhf];
+            lv[j] = wl[i * RH + rhf];
+            scv[j] = wsc[i * RH + rhf];
+            mloc = fmaxf(mloc, mv[j]);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if (lane == 0) red_m[wave] = mloc;
+    __syncthreads();
+    const float mstar = fmaxf(red_m[2 * fr], red_m[2 * fr + 1]);
+    float lloc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMPPer; ++j) {
+        const int i = ft + 128 * j;
+        if (frow && i < S) {
+            const float wgt = (mstar == -INFINITY || mv[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv[j] - mstar);
+            if (wgt != 0.f) lloc += wgt * lv[j];
+            fac_s[0][fr][i] = wgt != 0.f ? wgt * scv[j][0] : 0.f;
+            fac_s[1][fr][i] = wgt != 0.f ? wgt * scv[j][1] : 0.f;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) lloc += __shfl_xor(lloc, off);
+    if (lane == 0) red_l[wave] = lloc;
+    __syncthreads();
+
+    // weighted sums of this thread's splits (rows past the block weigh 0)
+    auto lo4 = [](u32x4 v) __attribute__((always_inline)) {
+        return __builtin_convertvector(__builtin_bit_cast(f16x4v, u32x2{v[0], v[1]}), f32x4);
+    };
+    auto hi4 = [](u32x4 v) __attribute__((always_inline)) {
+        return __builtin_convertvector(__builtin_bit_cast(f16x4v, u32x2{v[2], v[3]}), f32x4);
+    };
+    const float *f_s = fac_s[oc < 32 ? 0 : 1][pr];
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+    for (int u = 0; u < kMPBatch; ++u) {
+        const int i = sg + 2 * u;
+        const float wgt = prow && i < S ? f_s[i] : 0.f;
+        if (wgt != 0.f) {                              // unweighted splits may hold any bits
+            a0 += wgt * lo4(v0[u]);
+            a1 += wgt * hi4(v0[u]);
+        }
+    }
+    for (int i0 = sg + 2 * kMPBatch; i0 < S; i0 += 2 * kMPBatch) {
+        u32x4 v[kMPBatch];
+        float wt[kMPBatch];
+#pragma unroll
+        for (int u = 0; u < kMPBatch; ++u) {
+            const int i = i0 + 2 * u;
+            wt[u] = prow && i < S ? f_s[i] : 0.f;
+            v[u] = op[(int64_t)(i < S ? i : 0) * step8];
+        }
+#pragma unroll
+        for (int u = 0; u < kMPBatch; ++u)
+            if (wt[u] != 0.f) {
+                a0 += wt[u] * lo4(v[u]);
+                a1 += wt[u] * hi4(v[u]);
+            }
+    }
+    if (sg == 1) {
+        part_s[2 * pair] = a0;
+        part_s[2 * pair + 1] = a1;
+    }
+    __syncthreads();
+    if (sg == 0) {
+        a0 += part_s[2 * pair];
+        a1 += part_s[2 * pair + 1];
+        const float lsum = red_l[2 * pr] + red_l[2 * pr + 1];
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        f32x4 *dst = reinterpret_cast<f32x4 *>(&o_s[pr][8 * oc]);
+        dst[0] = a0 * inv;
+        dst[1] = a1 * inv;
+    }
+    __syncthreads();
+
+    // C[n][r] over this wave's reduction half: B column l16 = row l16 of the block
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        u32x4 bh = {0u, 0u, 0u, 0u}, bl = bh;
+        if (l16 < nrow) {
+            const int k = 256 * kh + 32 * s + 8 * g;
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&o_s[l16][k]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&o_s[l16][k + 4]);
+            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned ph = pack_p<KIND>(x[2 * j], x[2 * j + 1]);
+                bh[j] = ph;
+                bl[j] = pack_p<KIND>(x[2 * j] - unpack_lo<KIND>(ph), x[2 * j + 1] - unpack_lo<KIND>(ph >> 16));
+            }
+        }
+        acc = mfma16x16x32<KIND>(wv[s], bh, acc);
+        acc = mfma16x16x32<KIND>(wv[s], bl, acc);
+    }
+    if (kh == 1) acc_s[nb][lane] = acc;
+    __syncthreads();
+    if (kh == 0 && l16 < nrow) {                       // lane: outputs 16 nb + 4 g .. + 3 of row l16
+        acc += acc_s[nb][lane];
+        *reinterpret_cast<f32x4 *>(a.out + (int64_t)(r0 + l16) * a.out_rs + (int64_t)h * 128 + 64 * half + 16 * nb +
+                                   4 * g) = acc;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_merge_proj(const MergeProjArgs &a, int kind, hipStream_t stream) {
+    if (a.n_rows < 1 || a.n_head < 1 || a.n_split < 2 || a.n_split > kMaxSplits) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)((a.n_rows + kMPRows - 1) / kMPRows) * a.n_head;   // (row block, head)
+    const int64_t grid = 16 * ((blocks + 7) / 8);       // two column halves, x and x + 8
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    void (*kern)(MergeProjArgs) = kind == KV_BF16 ? merge_proj_kernel<KV_BF16>
+                                  : kind == KV_F16 ? merge_proj_kernel<KV_F16> : nullptr;
+    if (!kern) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMPThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_proj(const ProjArgs &p, int kind, bool a_f32, bool c_f32, hipStream_t stream) {
     if (p.M < 1 || p.H < 1 || p.N % kPCols || p.K % 128 || p.K > 4 * 32 * kSMaxSteps) return hipErrorInvalidValue;
