@@ -31,6 +31,10 @@
  *     for MLA_FA_ERR_HIP, which reports a failed launch.  No exceptions, no abort,
  *     no host synchronisation.  Calls are reentrant; calls that share a workspace
  *     must be ordered on one stream.
+ *   - A call enqueues kernel launches only (no memory set, copy or allocation), so a
+ *     call on a capturing stream is recorded into a HIP graph and its replays
+ *     reproduce the eager result bit for bit (mla_fa_decode_noalloc: call it once
+ *     outside capture first, which looks up the device's scratch address).
  *   - Element types: q is f16 or bf16 (bits, [..][n_head][576] contiguous); the
  *     cache is f16, bf16 or Q8_0.  Supported pairs: f16/f16, bf16/bf16, f16/Q8_0,
  *     bf16/Q8_0.  A Q8_0 row is 18 blocks of {f16 scale d, 32 int8 codes} = 612
