@@ -53,6 +53,10 @@ def ref_absorbed(p, rows=None):
     (dict(n_seq=8, n_tok=2, n_head=64, n_kv=900, q_type=BF16, kv_type=BF16, seed=10, causal=True), 3),
     (dict(n_seq=17, n_tok=1, n_head=32, n_kv=700, q_type=F16, kv_type=F16, seed=11), 5),
     (dict(n_seq=3, n_tok=1, n_head=128, n_kv=2000, q_type=BF16, kv_type=Q8, seed=12), 0),
+    # many splits: the fused merge's later load batches (more than 32 splits), and 1024
+    # splits over 2000 cells, where most splits are empty
+    (dict(n_seq=5, n_tok=1, n_head=64, n_kv=9000, q_type=BF16, kv_type=BF16, seed=13), 100),
+    (dict(n_seq=2, n_tok=1, n_head=16, n_kv=2000, q_type=F16, kv_type=F16, seed=14), 1024),
 ])
 def test_absorbed(kw, n_split):
     p = synth.make_absorbed_problem(**kw)
