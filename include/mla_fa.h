@@ -86,7 +86,9 @@ enum mla_fa_status {
 const char *mla_fa_strerror(int status);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: mla_fa_attend takes
- * per-token sparse index lists). */
+ * per-token sparse index lists; 2.1.0: mla_fa_absorbed fuses the split merge with the
+ * output projection, three launches per call, and mla_fa_attend splits rows of
+ * device-side lengths in proportion to those lengths). */
 int mla_fa_version(void);
 
 /*
@@ -228,7 +230,14 @@ int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64
  *   softcap  0 = off; > 0: the scaled score x = scale * q.k becomes
  *            softcap * tanh(x / softcap) before the mask bias is added.
  *   out      [n_seq][n_tok][n_head][512] fp32 (device).
- *   n_split / workspace as for decode with n_rows = n_seq * n_tok.
+ *   n_split / workspace as for decode with n_rows = n_seq * n_tok.  When the call
+ *            splits (n_split resolves to 2 or more), has kv_len or kv_idx, and
+ *            n_seq * n_tok <= 256, the rows' lengths are known on the device only, so
+ *            the kernels share the workspace's n_rows * n_split partial slots out in
+ *            proportion to them (long rows get more pieces, empty rows none; at most one
+ *            piece per workgroup the chip runs at once) instead of cutting every row
+ *            into n_split pieces: n_split then sets the workspace size, not a per-row
+ *            count.  The results differ only by floating-point reassociation.
  * Errors: as for decode; ERR_INVALID also for a negative or non-finite softcap, for
  * kv_len / alibi_slopes / sinks not 4-byte aligned, and for kv_idx with causal or kv_len.
  */

@@ -1,6 +1,7 @@
 // api.hip -- the extern "C" boundary of libmlafa: argument validation (before any HIP
 // call), split planning, workspace layout and launches.  See include/mla_fa.h for the
 // contract of every entry point.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -163,6 +164,7 @@ struct Common {
     const float *alibi = nullptr;
     const float *sinks = nullptr;
     float softcap = 0.f;
+    bool ragged_ok = false;        // the call runs its own merge: rows may share slots by length
 };
 
 int validate(const Common &c) {
@@ -203,6 +205,29 @@ int validate(const Common &c) {
     return MLA_FA_OK;
 }
 
+// Rows whose lengths only the device holds (valid lengths or index-list counts) get a
+// length-proportional plan when the call splits and runs its own merge: the kernel shares
+// the call's rows * n_split partial slots out by length (all but the last, which holds the
+// plan's row table), at most one piece per workgroup slot of the chip (kCUs / head groups
+// pieces, at least one per row).  With every row cut into n_split pieces instead, the
+// longest row's pieces set the call's time.
+Ragged ragged_for(const Common &c, const Plan &p) {
+    Ragged g;
+    std::memset(&g, 0, sizeof(g));
+    const int64_t rows = (int64_t)c.n_seq * c.n_tok;
+    if (!c.ragged_ok || p.n_split <= 1 || rows > kRaggedRows || (!c.kv_len && !c.kv_idx)) return g;
+    const int64_t slots = rows * p.n_split - 1;   // >= rows, as n_split >= 2
+    const int64_t chip = std::max<int64_t>(rows, kCUs / p.head_groups);
+    g.budget = (int)std::min(slots, chip);
+    g.kv_len = c.kv_idx ? nullptr : c.kv_len;
+    g.count = c.kv_idx ? c.kv_idx_count : nullptr;
+    g.n_kv = c.n_kv;
+    g.n_tok = c.n_tok;
+    g.causal = c.causal ? 1 : 0;
+    g.rows = (int)rows;
+    return g;
+}
+
 int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
     const int64_t n_rows = (int64_t)c.n_seq * c.n_tok;
     if (p.n_split > 1) {
@@ -241,17 +266,21 @@ int run_partials(const Common &c, const Plan &p, hipStream_t stream) {
     a.sinks = c.sinks;
     a.cap_in = c.softcap > 0.f ? c.scale / c.softcap : 0.f;
     a.cap_out = c.softcap * 1.4426950408889634f;
+    a.ragged = ragged_for(c, p);
+    if (a.ragged.budget)   // one launch, one workgroup per (piece, head group)
+        a.grid_x = p.head_groups > 1 ? 8 * p.head_groups * ((a.ragged.budget + 7) / 8) : a.ragged.budget;
     if (std::getenv("MLA_FA_LOG"))
-        fprintf(stderr, "mla_fa: rows=%lld heads=%d n_kv=%lld split=%d chunk=%lld shape=%d hg=%d grid=%dx%lld\n",
+        fprintf(stderr,
+                "mla_fa: rows=%lld heads=%d n_kv=%lld split=%d chunk=%lld shape=%d hg=%d grid=%dx%lld pieces=%d\n",
                 (long long)n_rows, c.n_head, (long long)c.n_kv, p.n_split, (long long)p.split_chunk,
-                p.shape, p.head_groups, p.grid_x, (long long)n_rows);
+                p.shape, p.head_groups, a.grid_x, a.ragged.budget ? 1LL : (long long)n_rows, a.ragged.budget);
     bool fail;
     hipError_t e = launch_skipped(&fail) ? skipped_status(fail) : launch_attention(a, kv_kind_of(c.kv_type), p.shape, stream);
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
 int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *ws, size_t ws_bytes,
-              hipStream_t stream, const float *sinks = nullptr) {
+              hipStream_t stream, const float *sinks = nullptr, const Ragged *ragged = nullptr) {
     if (n_split <= 1) return MLA_FA_OK;
     if (n_rows * n_head > 0x7FFFFFFFLL) return MLA_FA_ERR_INVALID;   // one merge workgroup per (row, head)
     const size_t need = partial_bytes(n_rows, n_head, n_split);
@@ -259,7 +288,7 @@ int run_merge(int64_t n_rows, int n_head, int n_split, float *out, const void *w
     bool fail;
     hipError_t e = launch_skipped(&fail) ? skipped_status(fail)
                                          : launch_merge((int)n_rows, n_head, n_split, static_cast<const float *>(ws),
-                                                        out, sinks, stream);
+                                                        out, sinks, ragged ? *ragged : Ragged{}, stream);
     return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;
 }
 
@@ -338,7 +367,7 @@ const char *mla_fa_strerror(int status) {
     return "unknown status";
 }
 
-int mla_fa_version(void) { return 20000; }
+int mla_fa_version(void) { return 20100; }
 
 int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type) {
     if (n_rows < 1 || n_kv < 1 || check_heads(n_head)) return 1;
@@ -462,6 +491,7 @@ int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_
     c.idx_tok_stride = idx_tok_stride;
     c.scale = scale; c.out = out; c.n_split = n_split; c.ws = workspace; c.ws_bytes = workspace_bytes;
     c.kv_len = kv_len; c.alibi = alibi_slopes; c.sinks = sinks; c.softcap = softcap;
+    c.ragged_ok = true;
     int st = validate(c);
     if (st) return st;
     const int64_t n_rows = (int64_t)n_seq * n_tok;
@@ -471,7 +501,8 @@ int mla_fa_attend(const void *q, int q_type, const void *kv, int kv_type, int64_
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_partials(c, p, s);
     if (st) return st;
-    return run_merge(n_rows, n_head, p.n_split, out, workspace, workspace_bytes, s, sinks);
+    const Ragged rg = ragged_for(c, p);
+    return run_merge(n_rows, n_head, p.n_split, out, workspace, workspace_bytes, s, sinks, &rg);
 }
 
 int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, int kv_type,

@@ -65,6 +65,169 @@ __device__ __forceinline__ int clamp_row(int v, int64_t n_kv) {
 }
 
 // ---------------------------------------------------------------------------------
+// Length-proportional split plan (Ragged with budget > 0).  One whole wave computes it,
+// lane l holding rows l + 64 i; every wave that needs the plan computes it itself from
+// the same lengths, so no workgroup waits for another.
+constexpr int kRaggedPer = kRaggedRows / 64;
+
+// End of row r's range (keys, or index-list positions), clamped as the row clamps it.
+__device__ __forceinline__ int64_t ragged_extent(const Ragged &g, int r) {
+    int64_t e;
+    if (g.count) {
+        e = g.count[r];
+    } else {
+        int64_t len = g.kv_len[r / g.n_tok];
+        len = len < 0 ? 0 : (len > g.n_kv ? g.n_kv : len);
+        e = g.causal ? len - g.n_tok + r % g.n_tok + 1 : len;
+    }
+    return e < 0 ? 0 : (e > g.n_kv ? g.n_kv : e);
+}
+
+struct RaggedPlan {
+    int pieces[kRaggedPer];    // pieces of rows lane + 64 i
+    int chunk;                 // tiles per piece (C), wave-uniform
+    int nper;                  // row blocks of 64 in use, wave-uniform
+};
+
+// Sum over the 64 lanes, in every lane: DPP rotations within each 16-lane row, then the
+// two cross-row swaps (VALU only; no LDS round trip).
+__device__ __forceinline__ int wave_sum_i32(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);   // row_ror:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);   // row_ror:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x122, 0xF, 0xF, false);   // row_ror:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x121, 0xF, 0xF, false);   // row_ror:1
+    auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = (int)s32[0] + (int)s32[1];
+    auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (int)s16[0] + (int)s16[1];
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xF, 0xF, false));
+    auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max((int)s32[0], (int)s32[1]);
+    auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return max((int)s16[0], (int)s16[1]);
+}
+
+// ceil(t / d) for 0 <= t, d < 2^26 with rd = 1 / d in double: the rounded quotient is
+// within 2^-26 of t / d, so its ceiling is exact except where t / d is an integer k and
+// the product lands just above k; the one check corrects that.
+__device__ __forceinline__ int ceil_div_small(int t, int d, double rd) {
+    const int q = (int)__builtin_ceil((double)t * rd);
+    return q > 0 && (q - 1) * d >= t ? q - 1 : q;
+}
+
+// C = the smallest chunk (in tiles) with sum_r ceil(tiles_r / C) <= budget.  It lies in
+// [ceil(T / B), ceil(T / (B - n))] (T tiles in all, n non-empty rows, B the budget: each
+// ceil adds less than one piece per row), and C = the longest row always fits (B >= rows),
+// so a bisection over that range, a few steps in practice, finds it.
+__device__ RaggedPlan ragged_plan(const Ragged &g) {
+    const int lane = threadIdx.x & 63;
+    RaggedPlan p;
+    p.nper = (g.rows + 63) >> 6;
+    int t[kRaggedPer];
+    int thi = 0, tlo = 0, nz = 0, mx = 0;      // the tile total as 2^16 thi + tlo (no overflow)
+#pragma unroll
+    for (int i = 0; i < kRaggedPer; ++i) {
+        const int r = lane + 64 * i;
+        t[i] = i < p.nper && r < g.rows ? (int)((ragged_extent(g, r) + kTileKeys - 1) / kTileKeys) : 0;
+        thi += t[i] >> 16;
+        tlo += t[i] & 0xFFFF;
+        nz += t[i] > 0;
+        mx = t[i] > mx ? t[i] : mx;
+    }
+    const long long tot = ((long long)__builtin_amdgcn_readfirstlane(wave_sum_i32(thi)) << 16) +
+                          __builtin_amdgcn_readfirstlane(wave_sum_i32(tlo));
+    nz = __builtin_amdgcn_readfirstlane(wave_sum_i32(nz));
+    mx = __builtin_amdgcn_readfirstlane(wave_max_i32(mx));
+    int lo = 1, hi = 1;
+    if (tot > 0) {
+        const long long b = g.budget;
+        lo = (int)((tot + b - 1) / b);
+        hi = mx;
+        if (b > nz) {
+            const long long h2 = (tot + (b - nz) - 1) / (b - nz);
+            if (h2 < hi) hi = (int)h2;
+        } else {
+            lo = mx;                                  // one piece per non-empty row
+        }
+        lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
+    }
+    while (lo < hi) {                                 // (lo, hi wave-uniform)
+        const int mid = (lo + hi) >> 1;
+        const double rd = 1.0 / mid;
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kRaggedPer; ++i)
+            if (i < p.nper) c += ceil_div_small(t[i], mid, rd);
+        if (__builtin_amdgcn_readfirstlane(wave_sum_i32(c)) <= g.budget) hi = mid;
+        else lo = mid + 1;
+    }
+    p.chunk = lo;
+    const double rd = 1.0 / lo;
+#pragma unroll
+    for (int i = 0; i < kRaggedPer; ++i) p.pieces[i] = i < p.nper ? ceil_div_small(t[i], lo, rd) : 0;
+    return p;
+}
+
+// Inclusive sum of x over lanes 0 .. lane.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Row and piece of the plan's piece number k; row = -1 when k is past the last piece.
+__device__ __forceinline__ void ragged_find(const RaggedPlan &p, int k, int &row, int &piece) {
+    int carry = 0;
+    row = -1;
+    piece = 0;
+#pragma unroll
+    for (int i = 0; i < kRaggedPer; ++i) {
+        if (i >= p.nper) break;
+        const int incl = wave_incl_scan(p.pieces[i]) + carry;
+        const int excl = incl - p.pieces[i];
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(k >= excl && k < incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            row = 64 * i + l;
+            piece = k - __builtin_amdgcn_readlane(excl, l);
+            break;
+        }
+        carry = __builtin_amdgcn_readlane(incl, 63);
+    }
+}
+
+// The plan's row table: one int32 per row, its first slot | its piece count << 16 (both
+// at most kRaggedRows).  It lives in the O area of the last partial slot, which the plan
+// never gives a piece (budget <= slots - 1); the first workgroup of the attention launch
+// writes it and the merge reads it.  Offset in floats from the workspace base.
+__device__ __forceinline__ int64_t ragged_table_off(int n_split, int rows, int heads) {
+    const int64_t cap = (int64_t)n_split * rows;                  // partial slots
+    return 4 * cap * heads + (cap - 1) * heads * (kDV / 2);       // m, l, scale[2]; then O
+}
+
+__device__ __forceinline__ void ragged_write_table(const RaggedPlan &p, int32_t *tab, int rows) {
+    const int lane = threadIdx.x & 63;
+    int carry = 0;
+#pragma unroll
+    for (int i = 0; i < kRaggedPer; ++i) {
+        if (i >= p.nper) break;
+        const int incl = wave_incl_scan(p.pieces[i]) + carry;
+        const int r = lane + 64 * i;
+        if (r < rows) tab[r] = (incl - p.pieces[i]) | (p.pieces[i] << 16);
+        carry = __builtin_amdgcn_readlane(incl, 63);
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // The attention kernel.  NW waves, each owning MB blocks of 16 heads; WK waves share
 // one head set and split every 64-key tile between them (WK = 2: keys 0..31 /
 // 32..63).  Heads per workgroup = NW / WK * 16 * MB.  IDX: sparse path (rows gathered
@@ -100,32 +263,67 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
     const int g = lane >> 4;                          // 16-lane group
     const int l16 = lane & 15;
 
-    // ---- which (row, split, head group) this workgroup owns
-    int hg, split;
-    if (a.head_groups > 1) {
-        // workgroups x and x+8 are dispatched to the same XCD (round-robin over 8);
-        // give them one key range and different head groups so they share its L2.
-        const int x = blockIdx.x;
-        hg = (x >> 3) % a.head_groups;
-        split = (x & 7) + 8 * (x / (8 * a.head_groups));
-    } else {
-        hg = 0;
-        split = blockIdx.x;
-    }
-    if (split >= a.n_split) return;
+    // ---- which (row, split, head group) this workgroup owns.  Workgroups x and x+8 are
+    // dispatched to the same XCD (round-robin over 8): they get one key range and
+    // different head groups, so they share its L2.
+    int hg, split, row;
+    int64_t slot;                                     // partial slot of (split, row)
+    int64_t kend, chunk = a.split_chunk;
     const int n_rows = a.n_seq * a.n_tok;
-    const int row_lin = (int)blockIdx.y + a.row_base;
-    const int s_idx = row_lin / a.n_tok;
-    const int t_idx = a.n_tok - 1 - row_lin % a.n_tok;   // longest causal rows first
-    const int row = s_idx * a.n_tok + t_idx;
+    {
+        const int x = blockIdx.x;
+        int xr = x;                                   // key range number
+        hg = 0;
+        if (a.head_groups > 1) {
+            hg = (x >> 3) % a.head_groups;
+            xr = (x & 7) + 8 * (x / (8 * a.head_groups));
+        }
+        if (a.ragged.budget) {
+            // length-proportional plan: key range xr is the plan's piece number xr, which
+            // is also its partial slot.  Wave 0 computes the plan and hands (row, piece,
+            // chunk) over in stage 1's index area, which no copy reaches before the main
+            // loop's first barrier; the first workgroup also writes the merge's row table.
+            int *hand = reinterpret_cast<int *>(lds + kStageBytes + kIdxOff);
+            if (wave == 0) {
+                const RaggedPlan p = ragged_plan(a.ragged);
+                int r, j;
+                ragged_find(p, xr, r, j);
+                if (lane == 0) {
+                    hand[0] = r;
+                    hand[1] = j;
+                    hand[2] = p.chunk;
+                }
+                if (x == 0)
+                    ragged_write_table(p, reinterpret_cast<int32_t *>(a.ws + ragged_table_off(a.n_split, n_rows, a.n_head)),
+                                       a.ragged.rows);
+            }
+            __syncthreads();
+            row = hand[0];
+            split = hand[1];
+            chunk = (int64_t)hand[2] * kTileKeys;
+            if (row < 0) return;
+            kend = ragged_extent(a.ragged, row);
+            slot = xr;
+        } else {
+            split = xr;
+            if (split >= a.n_split) return;
+            const int row_lin = (int)blockIdx.y + a.row_base;
+            const int t = a.n_tok - 1 - row_lin % a.n_tok;   // longest causal rows first
+            row = row_lin / a.n_tok * a.n_tok + t;
+            slot = (int64_t)split * n_rows + row;
+        }
+    }
+    const int s_idx = row / a.n_tok;
+    const int t_idx = row % a.n_tok;
     const uint8_t *kvs = a.kv + (int64_t)s_idx * a.kv_seq_stride;
     const uint16_t *mrow = a.mask ? a.mask + (int64_t)s_idx * a.mask_seq_stride +
                                         (int64_t)t_idx * a.mask_tok_stride
                                   : nullptr;
     const int32_t *irow = IDX ? a.kv_idx + (int64_t)s_idx * a.idx_seq_stride + (int64_t)t_idx * a.idx_tok_stride
                               : nullptr;
-    int64_t kend, chunk = a.split_chunk;
-    if constexpr (IDX) {
+    if (a.ragged.budget) {
+        // kend and chunk come from the plan
+    } else if constexpr (IDX) {
         const int64_t c = a.kv_idx_count[row];          // one count per (sequence, token) row
         kend = c < 0 ? 0 : (c > a.n_kv ? a.n_kv : c);
         chunk = (kend + a.n_split - 1) / a.n_split;
@@ -769,7 +967,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_kernel(AttnArgs a) {
         float *wl = wm + (int64_t)a.n_split * RH;
         float *wsc = wl + (int64_t)a.n_split * RH;                       // [split][row, head][half]
         uint16_t *wo = reinterpret_cast<uint16_t *>(wsc + 2 * (int64_t)a.n_split * RH);
-        const int64_t base = (int64_t)split * RH + (int64_t)row * a.n_head;
+        const int64_t base = slot * a.n_head;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int head_l = h_base + mb * 16 + l16;
@@ -1259,19 +1457,20 @@ __global__ void __launch_bounds__(NP * 128, 1) attn_pair_kernel(AttnArgs a) {
 // splits are read in one round trip, reduced to the factors in LDS, and the loads already
 // in flight are weighted (a select drops unweighted splits, whose values are read but
 // may hold any bits); later batches follow, and
-// the four split groups are summed through LDS.
-constexpr int kMergeThreads = 512;
-constexpr int kMergeGroups = kMergeThreads / 128;
+// the four split groups are summed through LDS.  Under a length-proportional plan
+// (Ragged) a row's pieces are the slots P_r .. P_r + n_r - 1 that the plan gives it; a row
+// with no piece outputs 0.
 constexpr int kMergeBatch = 8;
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_head, int n_split,
-                                                              const float *__restrict__ ws,
-                                                              float *__restrict__ out,
-                                                              const float *__restrict__ sinks) {
+template <int G>   // split groups of 128 threads
+__global__ void __launch_bounds__(128 * G) merge_kernel(int n_rows, int n_head, int n_split,
+                                                        const float *__restrict__ ws, float *__restrict__ out,
+                                                        const float *__restrict__ sinks, Ragged rg) {
+    constexpr int kThreads = 128 * G;
     __shared__ float w_s[kMaxSplits];
     __shared__ float l_s[kMaxSplits];
     __shared__ f32x2v sc_s[kMaxSplits];
-    __shared__ float red[kMergeThreads / 64];
-    __shared__ f32x4 part[kMergeGroups - 1][128];
+    __shared__ float red[kThreads / 64];
+    __shared__ f32x4 part[G - 1 > 0 ? G - 1 : 1][128];
     const int64_t rh = blockIdx.x;                    // row * n_head + head
     const int64_t RH = (int64_t)n_rows * n_head;
     const float *wm = ws;
@@ -1280,8 +1479,19 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     const uint16_t *wo = reinterpret_cast<const uint16_t *>(wsc + (int64_t)n_split * RH);
     const int tid = threadIdx.x;
     const int q = tid & 127, sg = tid >> 7;
-    const u32x2 *op = reinterpret_cast<const u32x2 *>(wo + rh * kDV) + q;   // 4 f16 values
-    const int64_t step4 = RH * kDV / 4;               // stride between splits, in quads
+    // (slot, head) entry of this row's first split, the stride between its splits, and
+    // their number
+    int64_t e0 = rh, es = RH;
+    int ns = n_split;
+    if (rg.budget) {
+        const unsigned v = reinterpret_cast<const unsigned *>(ws + ragged_table_off(n_split, n_rows, n_head))[rh / n_head];
+        const int first = (int)(v & 0xFFFFu), n = (int)(v >> 16);
+        e0 = (int64_t)(n > 0 ? first : 0) * n_head + rh % n_head;   // (no piece: slot 0, read and weighed 0)
+        es = n_head;
+        ns = n;
+    }
+    const u32x2 *op = reinterpret_cast<const u32x2 *>(wo + e0 * kDV) + q;   // 4 f16 values
+    const int64_t step4 = es * kDV / 4;               // stride between splits, in quads
     // O of a split = scale of its half x the stored f16 values
     auto f16x4_to_f32 = [](u32x2 v) __attribute__((always_inline)) {
         return __builtin_convertvector(__builtin_bit_cast(f16x4v, v), f32x4);
@@ -1290,15 +1500,15 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     u32x2 v0[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-        const int i = sg + u * kMergeGroups;
-        v0[u] = op[(int64_t)(i < n_split ? i : 0) * step4];   // unconditional: no wait until used
+        const int i = sg + u * G;
+        v0[u] = op[(int64_t)(i < ns ? i : 0) * step4];   // unconditional: no wait until used
     }
     float mloc = -INFINITY;
-    for (int i = tid; i < n_split; i += kMergeThreads) {
-        const float mi = wm[i * RH + rh];
+    for (int i = tid; i < ns; i += kThreads) {
+        const float mi = wm[e0 + i * es];
         w_s[i] = mi;
-        l_s[i] = wl[i * RH + rh];
-        sc_s[i] = wsc[i * RH + rh];
+        l_s[i] = wl[e0 + i * es];
+        sc_s[i] = wsc[e0 + i * es];
         mloc = fmaxf(mloc, mi);
     }
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
@@ -1306,10 +1516,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     __syncthreads();
     float mstar = red[0];
 #pragma unroll
-    for (int i = 1; i < kMergeThreads / 64; ++i) mstar = fmaxf(mstar, red[i]);
+    for (int i = 1; i < kThreads / 64; ++i) mstar = fmaxf(mstar, red[i]);
     // weights 2^(m_i - m*) (0 for empty splits, and for every split if all are empty)
     float lloc = 0.f;
-    for (int i = tid; i < n_split; i += kMergeThreads) {
+    for (int i = tid; i < ns; i += kThreads) {
         const float mi = w_s[i];
         const float wgt = (mstar == -INFINITY || mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - mstar);
         if (wgt != 0.f) lloc += wgt * l_s[i];
@@ -1323,7 +1533,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     __syncthreads();
     float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMergeThreads / 64; ++i) lsum += red[i];
+    for (int i = 0; i < kThreads / 64; ++i) lsum += red[i];
     if (sinks && mstar != -INFINITY)   // the sink joins the normaliser (m* in log2 units)
         lsum += __builtin_amdgcn_exp2f(sinks[rh % n_head] * 1.4426950408889634f - mstar);
 
@@ -1331,19 +1541,19 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-        const int i = sg + u * kMergeGroups;
-        const float wgt = i < n_split ? f_s[i] : 0.f;
+        const int i = sg + u * G;
+        const float wgt = i < ns ? f_s[i] : 0.f;
         const f32x4 x = f16x4_to_f32(v0[u]);
         if (wgt != 0.f) acc += wgt * x;
     }
-    int i = sg + kMergeBatch * kMergeGroups;
-    for (; i + (kMergeBatch - 1) * kMergeGroups < n_split; i += kMergeBatch * kMergeGroups) {
+    int i = sg + kMergeBatch * G;
+    for (; i + (kMergeBatch - 1) * G < ns; i += kMergeBatch * G) {
         u32x2 v[kMergeBatch];
         float wv[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
-            wv[u] = f_s[i + u * kMergeGroups];
-            v[u] = op[(int64_t)(i + u * kMergeGroups) * step4];
+            wv[u] = f_s[i + u * G];
+            v[u] = op[(int64_t)(i + u * G) * step4];
         }
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {   // unweighted splits may hold any bits: select
@@ -1351,7 +1561,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
             if (wv[u] != 0.f) acc += wv[u] * x;
         }
     }
-    for (; i < n_split; i += kMergeGroups) {
+    for (; i < ns; i += G) {
         const float wgt = f_s[i];
         if (wgt != 0.f) acc += wgt * f16x4_to_f32(op[(int64_t)i * step4]);
     }
@@ -1359,17 +1569,17 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int n_rows, int n_
     __syncthreads();
     if (sg == 0) {
 #pragma unroll
-        for (int k = 0; k < kMergeGroups - 1; ++k) acc += part[k][q];
+        for (int k = 0; k < G - 1; ++k) acc += part[k][q];
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         reinterpret_cast<f32x4 *>(out + rh * kDV)[q] = acc * inv;
     }
 }
 
 // One launch per kMaxGridY query rows (the grid's y extent); a.row_base tells each launch
-// where its rows start.
+// where its rows start.  A length-proportional plan is one launch with y = 1.
 template <typename K>
 hipError_t launch_rows(K kernel, const AttnArgs &a, int threads, hipStream_t stream) {
-    const int64_t rows = (int64_t)a.n_seq * a.n_tok;
+    const int64_t rows = a.ragged.budget ? 1 : (int64_t)a.n_seq * a.n_tok;
     for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridY) {
         AttnArgs b = a;
         b.row_base = (int)r0;
@@ -1386,8 +1596,11 @@ hipError_t launch_one(const AttnArgs &a, hipStream_t stream) {
     return launch_rows(attn_kernel<MB, NW, WK, KIND, IDX>, a, NW * 64, stream);
 }
 
-// Per-sequence lengths, ALiBi, sinks and softcap run in the single-wave kernel only.
-bool uses_extras(const AttnArgs &a) { return a.kv_len || a.alibi || a.sinks || a.cap_in != 0.f; }
+// Per-sequence lengths, ALiBi, sinks, softcap and length-proportional plans run in the
+// single-wave kernel only.
+bool uses_extras(const AttnArgs &a) {
+    return a.kv_len || a.alibi || a.sinks || a.cap_in != 0.f || a.ragged.budget;
+}
 
 template <int NP, int KIND, bool IDX>
 hipError_t launch_pair(const AttnArgs &a, hipStream_t stream) {
@@ -1432,9 +1645,16 @@ hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream
 }
 
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
-                        const float *sinks, hipStream_t stream) {
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((int64_t)n_rows * n_head)), dim3(kMergeThreads), 0,
-                       stream, n_rows, n_head, n_split, ws, out, sinks);
+                        const float *sinks, const Ragged &ragged, hipStream_t stream) {
+    // Four split groups per (row, head), or two when that lets every workgroup of the
+    // launch be resident at once (up to 8,192 waves on the chip).
+    const int64_t pairs = (int64_t)n_rows * n_head;
+    if (pairs > 1024 && pairs <= 2048)
+        hipLaunchKernelGGL(merge_kernel<2>, dim3((unsigned)pairs), dim3(256), 0, stream, n_rows, n_head, n_split,
+                           ws, out, sinks, ragged);
+    else
+        hipLaunchKernelGGL(merge_kernel<4>, dim3((unsigned)pairs), dim3(512), 0, stream, n_rows, n_head, n_split,
+                           ws, out, sinks, ragged);
     return hipGetLastError();
 }
 

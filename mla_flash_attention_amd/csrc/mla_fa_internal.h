@@ -20,6 +20,23 @@ enum KvKind { KV_BF16 = 0, KV_F16 = 1, KV_Q8 = 2 };
 // (NW / WK) * 16 * MB.  P*: pair kernel (16-bit caches only), 32 heads per wave pair.
 enum Shape { SHAPE_H16 = 0, SHAPE_H32 = 1, SHAPE_H64 = 2, SHAPE_H128 = 3, SHAPE_P64 = 4, SHAPE_P128 = 5 };
 
+// Rows whose lengths only the device holds (per-sequence valid lengths, or index-list
+// counts) can share the call's partial slots in proportion to their lengths instead of
+// splitting every row into n_split pieces (budget > 0).  Each piece then covers at most C
+// tiles, C the smallest value with sum over rows of ceil(tiles / C) <= budget, and piece j
+// of row r fills partial slot P_r + j, P_r the pieces of rows 0 .. r-1.  The attention
+// launch derives the plan from the lengths and leaves a row table (P_r, pieces of r) in the
+// last partial slot, which no piece uses; the merge reads it.
+constexpr int kRaggedRows = 256;         // rows such a plan can hold
+struct Ragged {
+    const int32_t *kv_len;         // [n_seq] valid cells, or nullptr
+    const int32_t *count;          // [n_seq * n_tok] index-list lengths, or nullptr
+    int64_t n_kv;
+    int n_tok, causal;
+    int rows;                      // n_seq * n_tok, at most kRaggedRows
+    int budget;                    // pieces (at most rows * n_split - 1); 0 = no such plan
+};
+
 struct AttnArgs {
     const uint16_t *q;             // [n_seq][n_tok][n_head][576]
     const uint8_t *kv;             // byte base of the cache
@@ -50,12 +67,16 @@ struct AttnArgs {
     float cap_out;                 //   cap_in = 0 means no softcap
     int row_base;                  // query row of blockIdx.y = 0 (launches cover at most
                                    //   kMaxGridY rows each)
+    Ragged ragged;                 // budget > 0: length-proportional pieces, one launch,
+                                   //   blockIdx.x = piece (and head group)
 };
 constexpr int kMaxGridY = 65535;   // rows per launch (the grid's y extent)
 
 // Split partials inside the workspace, for R = n_seq*n_tok rows, H heads, S splits, in
 // this order: m [S][R][H] fp32 (log2 units), l [S][R][H] fp32, scale [S][R][H][2] fp32,
-// O [S][R][H][512] f16.  O is the unnormalised output, each 256-column half stored times
+// O [S][R][H][512] f16 (slot = split * R + row; under a length-proportional plan slot =
+// P_r + piece, the [S][R] slots read as one list).  O is the unnormalised output, each
+// 256-column half stored times
 // 2^(15 - e) where max |O| < 2^e over the half (the scale kept is 2^(e - 15)), so every
 // value keeps f16's relative precision (2^-11) whatever the magnitude of the cache's
 // values.
@@ -111,7 +132,7 @@ hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream
 hipError_t launch_merge_proj(const MergeProjArgs &a, int kind, hipStream_t stream);
 hipError_t launch_proj(const ProjArgs &p, int kind, bool a_f32, bool c_f32, hipStream_t stream);
 hipError_t launch_merge(int n_rows, int n_head, int n_split, const float *ws, float *out,
-                        const float *sinks, hipStream_t stream);
+                        const float *sinks, const Ragged &ragged, hipStream_t stream);
 hipError_t launch_mha(const MhaArgs &a, int kv_kind, hipStream_t stream);
 hipError_t launch_compact(const uint16_t *mask, int64_t mask_row_stride, int n_rows, int64_t n_kv,
                           int32_t *idx, int64_t idx_row_stride, int32_t *count,

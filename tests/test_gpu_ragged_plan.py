@@ -1,0 +1,84 @@
+"""GPU parity of split calls whose rows carry device-side lengths (mla_fa_attend with
+per-sequence valid lengths, or with per-row index lists).  Such calls share their
+rows x n_split partial slots out in proportion to the rows' lengths, on the device; these
+cases drive that plan to its corners: one long row among empty ones (it takes nearly every
+slot), every row empty, the largest row count the plan holds (one piece per row) and one
+row past it (the even split), an explicit split count far above what the chip needs, and
+index lists of very different lengths.  Whole outputs against the oracle at the usual
+bar: relative L2 <= 5e-3, max |error| <= 2e-2."""
+import numpy as np
+import pytest
+
+import oracle
+from mla_flash_attention_amd import synth
+from tests.gpu_common import assert_parity, to_dev
+from tests.test_gpu_attend import run_attend
+from tests.test_gpu_sparse_tokens import check as check_sparse
+
+pytestmark = pytest.mark.gpu
+
+BF16, F16, Q8 = synth.TYPE_BF16, synth.TYPE_F16, synth.TYPE_Q8_0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from mla_flash_attention_amd import binding
+    binding.lib()
+
+
+def _with_lengths(lengths, n_split=0, **kw):
+    lengths = np.asarray(lengths, dtype=np.int32)
+    p = synth.make_problem(kind="decode", n_seq=lengths.size, **kw)
+    p.kv_len = lengths
+    got = run_attend(p, n_split=n_split)
+    return p, got, oracle.attention_problem(p)
+
+
+@pytest.mark.parametrize("kv_type", [BF16, Q8])
+def test_one_long_row_among_empty(kv_type):
+    """Rows of 0, 0, 5000, 0 and 1 cells: the long row takes all but one of the pieces."""
+    p, got, ref = _with_lengths([0, 0, 5000, 0, 1], n_head=64, n_kv=5000, seed=61, kv_type=kv_type,
+                                q_type=BF16)
+    assert_parity(got, ref, f"one long row kv{kv_type}")
+    rows = got.reshape(p.n_seq, p.n_head, synth.DV)
+    assert np.all(rows[[0, 1, 3]] == 0)
+
+
+def test_every_row_empty():
+    p, got, ref = _with_lengths([0, 0, 0], n_head=128, n_kv=700, seed=62, sinks=True)
+    assert np.all(got == 0)
+    assert_parity(got, ref, "all empty")
+
+
+@pytest.mark.parametrize("n_seq,n_tok", [(128, 2), (257, 1)])
+def test_row_count_limit(n_seq, n_tok):
+    """256 causal rows (one piece each: the plan's budget equals the row count) and 257
+    rows (past the plan's limit: every row split evenly instead)."""
+    p = synth.make_problem(kind="decode", n_seq=n_seq, n_tok=n_tok, n_head=16, n_kv=300, seed=63, ragged=True,
+                           causal=n_tok > 1)
+    got = run_attend(p, n_split=2)
+    assert_parity(got, oracle.attention_problem(p), f"{n_seq}x{n_tok} rows")
+
+
+def test_split_count_far_above_the_chip():
+    """n_split = 200 for 6 rows: the plan still keeps one piece per workgroup slot."""
+    p = synth.make_problem(kind="decode", n_seq=3, n_tok=2, n_head=128, n_kv=9000, seed=64, ragged=True,
+                           causal=True, sinks=True, softcap=30.0)
+    got = run_attend(p, n_split=200)
+    assert_parity(got, oracle.attention_problem(p), "n_split 200")
+
+
+@pytest.mark.parametrize("kv_type", [BF16, Q8])
+def test_index_lists_of_different_lengths(kv_type):
+    """Per-token index lists of ~all, ~half, a few and no cells in one call."""
+    p = synth.make_problem(kind="sparse", n_seq=2, n_tok=2, n_head=64, n_kv=6000, q_type=BF16, kv_type=kv_type,
+                           seed=65)
+    g = np.random.default_rng(65)
+    keep = [g.random(p.n_kv) < f for f in (0.97, 0.5, 0.003, 0.0)]
+    for r, k in enumerate(keep):
+        s, t = divmod(r, p.n_tok)
+        p.mask[s, t] = np.where(k, np.uint16(0), np.uint16(synth.F16_NEG_INF))
+    check_sparse(p, f"uneven lists kv{kv_type}")
