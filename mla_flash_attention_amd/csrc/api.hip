@@ -207,16 +207,15 @@ int validate(const Common &c) {
 
 // Rows whose lengths only the device holds (valid lengths or index-list counts) get a
 // length-proportional plan when the call splits and runs its own merge: the kernel shares
-// the call's rows * n_split partial slots out by length (all but the last, which holds the
-// plan's row table), at most one piece per workgroup slot of the chip (kCUs / head groups
-// pieces, at least one per row).  With every row cut into n_split pieces instead, the
-// longest row's pieces set the call's time.
+// the call's rows * n_split partial slots out by length, at most one piece per workgroup
+// slot of the chip (kCUs / head groups pieces, at least one per row).  With every row cut
+// into n_split pieces instead, the longest row's pieces set the call's time.
 Ragged ragged_for(const Common &c, const Plan &p) {
     Ragged g;
     std::memset(&g, 0, sizeof(g));
     const int64_t rows = (int64_t)c.n_seq * c.n_tok;
     if (!c.ragged_ok || p.n_split <= 1 || rows > kRaggedRows || (!c.kv_len && !c.kv_idx)) return g;
-    const int64_t slots = rows * p.n_split - 1;   // >= rows, as n_split >= 2
+    const int64_t slots = rows * p.n_split;
     const int64_t chip = std::max<int64_t>(rows, kCUs / p.head_groups);
     g.budget = (int)std::min(slots, chip);
     g.kv_len = c.kv_idx ? nullptr : c.kv_len;

@@ -206,12 +206,11 @@ __device__ __forceinline__ void ragged_find(const RaggedPlan &p, int k, int &row
 }
 
 // The plan's row table: one int32 per row, its first slot | its piece count << 16 (both
-// at most kRaggedRows).  It lives in the O area of the last partial slot, which the plan
-// never gives a piece (budget <= slots - 1); the first workgroup of the attention launch
-// writes it and the merge reads it.  Offset in floats from the workspace base.
+// at most kRaggedRows), in the workspace's tail after the partials.  The first workgroup
+// of the attention launch writes it and the merge reads it.  Offset in floats from the
+// workspace base.
 __device__ __forceinline__ int64_t ragged_table_off(int n_split, int rows, int heads) {
-    const int64_t cap = (int64_t)n_split * rows;                  // partial slots
-    return 4 * cap * heads + (cap - 1) * heads * (kDV / 2);       // m, l, scale[2]; then O
+    return (int64_t)n_split * rows * heads * (int64_t)(kPartialEntryBytes / sizeof(float));
 }
 
 __device__ __forceinline__ void ragged_write_table(const RaggedPlan &p, int32_t *tab, int rows) {

@@ -26,7 +26,7 @@ enum Shape { SHAPE_H16 = 0, SHAPE_H32 = 1, SHAPE_H64 = 2, SHAPE_H128 = 3, SHAPE_
 // tiles, C the smallest value with sum over rows of ceil(tiles / C) <= budget, and piece j
 // of row r fills partial slot P_r + j, P_r the pieces of rows 0 .. r-1.  The attention
 // launch derives the plan from the lengths and leaves a row table (P_r, pieces of r) in the
-// last partial slot, which no piece uses; the merge reads it.
+// workspace's tail after the partials; the merge reads it.
 constexpr int kRaggedRows = 256;         // rows such a plan can hold
 struct Ragged {
     const int32_t *kv_len;         // [n_seq] valid cells, or nullptr
@@ -34,7 +34,7 @@ struct Ragged {
     int64_t n_kv;
     int n_tok, causal;
     int rows;                      // n_seq * n_tok, at most kRaggedRows
-    int budget;                    // pieces (at most rows * n_split - 1); 0 = no such plan
+    int budget;                    // pieces (at most rows * n_split); 0 = no such plan
 };
 
 struct AttnArgs {
@@ -75,13 +75,15 @@ constexpr int kMaxGridY = 65535;   // rows per launch (the grid's y extent)
 // Split partials inside the workspace, for R = n_seq*n_tok rows, H heads, S splits, in
 // this order: m [S][R][H] fp32 (log2 units), l [S][R][H] fp32, scale [S][R][H][2] fp32,
 // O [S][R][H][512] f16 (slot = split * R + row; under a length-proportional plan slot =
-// P_r + piece, the [S][R] slots read as one list).  O is the unnormalised output, each
-// 256-column half stored times
+// P_r + piece, the [S][R] slots read as one list), then a 1 KiB tail that holds that
+// plan's row table.  O is the unnormalised output, each 256-column half stored times
 // 2^(15 - e) where max |O| < 2^e over the half (the scale kept is 2^(e - 15)), so every
 // value keeps f16's relative precision (2^-11) whatever the magnitude of the cache's
 // values.
+constexpr size_t kPartialEntryBytes = 4 * sizeof(float) + kDV * sizeof(uint16_t);   // 1040
+constexpr size_t kRaggedTableBytes = kRaggedRows * sizeof(int32_t);
 inline size_t partial_bytes(int64_t rows, int heads, int splits) {
-    return (size_t)splits * rows * heads * (4 * sizeof(float) + kDV * sizeof(uint16_t));
+    return (size_t)splits * rows * heads * kPartialEntryBytes + kRaggedTableBytes;
 }
 
 // Per-head attention with separate K (192 wide) and V (128 wide), 16-bit types.

@@ -82,3 +82,26 @@ def test_index_lists_of_different_lengths(kv_type):
         s, t = divmod(r, p.n_tok)
         p.mask[s, t] = np.where(k, np.uint16(0), np.uint16(synth.F16_NEG_INF))
     check_sparse(p, f"uneven lists kv{kv_type}")
+
+
+def test_workspace_redzones():
+    """The plan's pieces and its row table stay inside a workspace of exactly
+    mla_fa_workspace_size bytes, and the output inside its buffer."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="decode", n_seq=5, n_tok=2, n_head=128, n_kv=4000, seed=66, ragged=True,
+                           causal=True)
+    rows, pad = p.n_seq * p.n_tok, 4096
+    n_out = rows * p.n_head * synth.DV
+    obuf = torch.full((n_out + 2 * pad,), 12345.0, dtype=torch.float32, device="cuda")
+    out = obuf[pad:pad + n_out].view(p.n_seq, p.n_tok, p.n_head, synth.DV)
+    ws_bytes = B.mla_fa_workspace_size(rows, p.n_head, p.n_kv, p.kv_type, 0)
+    wbuf = torch.full((ws_bytes + 2 * pad,), 77, dtype=torch.uint8, device="cuda")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    B.mla_fa_attend(to_dev(p.q), p.q_type, to_dev(p.kv), p.kv_type, p.scale, out, kv_len=f(p.kv_len), causal=True,
+                    n_split=0, workspace=wbuf[pad:pad + ws_bytes])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, synth.DV).astype(np.float64)
+    assert_parity(got, oracle.attention_problem(p), "redzones")
+    assert torch.all(obuf[:pad] == 12345.0) and torch.all(obuf[-pad:] == 12345.0)
+    assert torch.all(wbuf[:pad] == 77) and torch.all(wbuf[-pad:] == 77)
