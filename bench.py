@@ -27,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -120,12 +121,27 @@ def _dev(a):
     return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
 
 
-def _source_hash():
-    """Hash of the sources that decide the split-attention kernel and its launch."""
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def _code_only(text):
+    """C++ source without its comments and with runs of whitespace collapsed, so that an
+    edit to comments alone leaves the hash (and the measurements keyed by it) valid.
+    (These sources hold no string literal with a comment marker in it.)"""
+    return " ".join(_COMMENT.sub(" ", text).split())
+
+
+def _source_hash(files=None):
+    """Hash of the code (comments and layout aside) of the sources that decide the
+    split-attention kernels and their launches."""
     h = hashlib.sha256()
     for f in ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h", "device_common.h"):
-        with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if files is None:
+            with open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f)) as fh:
+                text = fh.read()
+        else:
+            text = files[f]
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

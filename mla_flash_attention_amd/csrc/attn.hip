@@ -66,8 +66,9 @@ __device__ __forceinline__ int clamp_row(int v, int64_t n_kv) {
 
 // ---------------------------------------------------------------------------------
 // Length-proportional split plan (Ragged with budget > 0).  One whole wave computes it,
-// lane l holding rows l + 64 i; every wave that needs the plan computes it itself from
-// the same lengths, so no workgroup waits for another.
+// lane l holding rows l + 64 i: wave 0 of every attention workgroup, from the same
+// lengths, so no workgroup waits for another; the merge reads the row table the first
+// workgroup leaves in the workspace.
 constexpr int kRaggedPer = kRaggedRows / 64;
 
 // End of row r's range (keys, or index-list positions), clamped as the row clamps it.

@@ -34,6 +34,23 @@ def test_traffic_tracks_the_kernel_sources(tmp_path, monkeypatch):
     assert bench._traffic("missing") is None
 
 
+def test_source_hash_ignores_comments_not_code():
+    """The traffic key covers the kernels' code: a comment or layout edit keeps it, any
+    change to code (a constant, an operator) changes it."""
+    names = ("attn.hip", "compact.hip", "api.hip", "mla_fa_internal.h", "device_common.h")
+    src = {f: open(os.path.join(ROOT, "mla_flash_attention_amd", "csrc", f)).read() for f in names}
+    h = bench._source_hash(src)
+    assert h == bench._source_hash()
+    edited = dict(src)
+    edited["attn.hip"] = "// a new note\n/* and a\n   block */\n" + src["attn.hip"].replace("\n", "\n\n", 5)
+    assert bench._source_hash(edited) == h
+    for old, new in (("kRescaleThresh = 8.0f", "kRescaleThresh = 9.0f"), ("x += __builtin_amdgcn", "x -= __builtin_amdgcn")):
+        assert old in src["attn.hip"]
+        changed = dict(src)
+        changed["attn.hip"] = src["attn.hip"].replace(old, new, 1)
+        assert bench._source_hash(changed) != h
+
+
 def _counter_csv(path, rows):
     import csv
     path.mkdir(parents=True)
