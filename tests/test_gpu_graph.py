@@ -28,10 +28,11 @@ def _gpu():
     binding.lib()
 
 
-def check_replays(call, outputs, extra=None):
+def check_replays(call, outputs, extra=None, scratch=()):
     """call(): the launches to capture; outputs: tensors the call writes (any dtype),
     compared whole; extra(): an additional check after every replay (for outputs only
-    partly defined, such as an index list past its count)."""
+    partly defined, such as an index list past its count); scratch: buffers the call
+    uses internally (a workspace), filled with junk before every replay."""
     import torch
     call()                                               # eager, on the current stream
     torch.cuda.synchronize()
@@ -47,6 +48,8 @@ def check_replays(call, outputs, extra=None):
             else:
                 o.fill_(-7)
         junk.fill_(float(k))
+        for t in scratch:
+            t.fill_(0x5A + k)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -134,3 +137,34 @@ def test_graph_absorbed_decode(n_split):
     ref = oracle.absorbed_attention(p.q_nope, p.q_pe, p.q_type, p.w_uk, p.w_uv, p.kv, p.kv_type, p.n_seq, p.n_tok,
                                     p.n_head, p.n_kv, p.scale)
     assert_parity(got.numpy().astype(np.float64).reshape(-1, 128), ref, f"graph absorbed n_split={n_split}")
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_graph_ragged_attend(sparse):
+    """mla_fa_attend over rows of device-side lengths: the length-proportional plan, its
+    row table in the workspace tail and the merge that reads it, replayed with the
+    workspace overwritten by junk before every replay."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    f = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if sparse:
+        p = synth.make_problem(kind="sparse", n_seq=2, n_tok=2, n_head=128, n_kv=7000, q_type=BF16, kv_type=Q8,
+                               seed=87)
+        rows = p.n_seq * p.n_tok
+        idx = torch.zeros((p.n_seq, p.n_tok, p.n_kv), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((p.n_seq, p.n_tok), dtype=torch.int32, device="cuda")
+        B.fa_mask_compact(to_dev(p.mask.reshape(rows, p.n_kv)), idx.view(rows, p.n_kv), cnt.view(rows))
+        extra_args = dict(mask=to_dev(p.mask), kv_idx=idx, kv_idx_count=cnt)
+    else:
+        p = synth.make_problem(kind="decode", n_seq=5, n_tok=2, n_head=128, n_kv=9000, q_type=BF16, kv_type=BF16,
+                               seed=88, ragged=True, causal=True, sinks=True, softcap=30.0)
+        rows = p.n_seq * p.n_tok
+        extra_args = dict(kv_len=f(p.kv_len), causal=True, sinks=f(p.sinks), softcap=p.softcap)
+    q, kv = to_dev(p.q), to_dev(p.kv)
+    out = torch.empty((p.n_seq, p.n_tok, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    ws = B.workspace_for(rows, p.n_head, p.n_kv, p.kv_type, 0)
+    assert ws is not None
+    (got,) = check_replays(lambda: B.mla_fa_attend(q, p.q_type, kv, p.kv_type, p.scale, out, n_split=0, workspace=ws,
+                                                   **extra_args), [out], scratch=[ws])
+    assert_parity(got.numpy().reshape(-1, synth.DV).astype(np.float64), oracle.attention_problem(p),
+                  f"graph ragged attend sparse={sparse}")

@@ -1,8 +1,9 @@
 """The library's calls are reentrant: host threads may call it at the same time, each
-on its own stream with its own workspace.  Four threads run a mix of calls (split
-decode, sparse step with chunked compaction, absorbed decode, per-head prefill) ten
-times each on their own streams; every result must equal the same call made alone,
-bit for bit (the kernels are deterministic), and the lone results meet the oracle bar."""
+on its own stream with its own workspace.  Five threads run a mix of calls (split
+decode, sparse step with chunked compaction, absorbed decode, per-head prefill, ragged
+multi-token attend) ten times each on their own streams; every result must equal the
+same call made alone, bit for bit (the kernels are deterministic), and the lone results
+meet the oracle bar."""
 import threading
 
 import numpy as np
@@ -96,9 +97,26 @@ def _mha_job(seed):
                                           "threads mha")
 
 
+def _ragged_job(seed):
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="decode", n_seq=4, n_tok=2, n_head=128, n_kv=6000, q_type=BF16, kv_type=BF16,
+                           seed=seed, ragged=True, causal=True)
+    q, kv = to_dev(p.q), to_dev(p.kv)
+    kvl = torch.from_numpy(np.ascontiguousarray(p.kv_len)).cuda()
+    out = torch.empty((p.n_seq, p.n_tok, p.n_head, synth.DV), dtype=torch.float32, device="cuda")
+    ws = B.workspace_for(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type, 0)
+
+    def run():
+        B.mla_fa_attend(q, p.q_type, kv, p.kv_type, p.scale, out, kv_len=kvl, causal=True, n_split=0, workspace=ws)
+        return [out]
+    return run, lambda got: assert_parity(got[0].cpu().numpy().reshape(-1, synth.DV).astype(np.float64),
+                                          oracle.attention_problem(p), "threads ragged")
+
+
 def test_concurrent_host_threads():
     import torch
-    jobs = [_decode_job(111), _sparse_job(112), _absorbed_job(113), _mha_job(114)]
+    jobs = [_decode_job(111), _sparse_job(112), _absorbed_job(113), _mha_job(114), _ragged_job(115)]
     alone = []
     for run, check in jobs:                            # each call alone, on the default stream
         got = [t.clone() for t in run()]
