@@ -87,8 +87,8 @@ const char *mla_fa_strerror(int status);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: mla_fa_attend takes
  * per-token sparse index lists; 2.1.0: mla_fa_absorbed fuses the split merge with the
- * output projection, three launches per call, and mla_fa_attend splits rows of
- * device-side lengths in proportion to those lengths). */
+ * output projection, three launches per call; mla_fa_attend and mla_fa_absorbed split
+ * rows of device-side lengths in proportion to those lengths). */
 int mla_fa_version(void);
 
 /*
@@ -305,8 +305,9 @@ int mla_fa_prefill_mha(const void *q, int q_type, const void *k, const void *v, 
  * Three launches on `stream`: the query projection (with the q_pe copy), the attention,
  * then the output projection, which for a split plan is fused with the merge of the
  * split partials (the epilogue reads the partials and W_UV; the merged latent output
- * never reaches memory).  Errors as for mla_fa_attend; ERR_WORKSPACE when the workspace
- * is missing or short.
+ * never reaches memory).  With kv_len, a split plan shares its partial slots out by the
+ * rows' lengths as mla_fa_attend does.  Errors as for mla_fa_attend; ERR_WORKSPACE when
+ * the workspace is missing or short.
  */
 size_t mla_fa_absorbed_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, int n_split);
 int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void *w_uk, const void *w_uv,

@@ -164,7 +164,8 @@ struct Common {
     const float *alibi = nullptr;
     const float *sinks = nullptr;
     float softcap = 0.f;
-    bool ragged_ok = false;        // the call runs its own merge: rows may share slots by length
+    bool ragged_ok = false;        // the call runs its own merge (which reads the plan's row
+                                   //   table): rows may share slots by length
 };
 
 int validate(const Common &c) {
@@ -580,6 +581,7 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
     c.scale = scale; c.out = ws ? reinterpret_cast<float *>(ws + lay.o_off) : nullptr; c.n_split = p.n_split;
     c.ws = ws ? ws + lay.part_off : nullptr; c.ws_bytes = lay.total - lay.part_off;
     c.kv_len = kv_len;
+    c.ragged_ok = true;            // merge_proj_kernel follows a length-proportional plan
     if (!workspace || workspace_bytes < lay.total) {
         // report argument errors first: validate with stand-in buffers
         Common v = c;
@@ -607,6 +609,7 @@ int mla_fa_absorbed(const void *q_nope, const void *q_pe, int q_type, const void
         ma.w = static_cast<const uint16_t *>(w_uv);
         ma.out = out; ma.out_rs = (int64_t)n_head * 128;
         ma.n_rows = (int)n_rows; ma.n_head = n_head; ma.n_split = p.n_split;
+        ma.ragged = ragged_for(c, p).budget > 0;
         bool fail;
         const hipError_t e = launch_skipped(&fail) ? skipped_status(fail) : launch_merge_proj(ma, kind, s);
         return e == hipSuccess ? MLA_FA_OK : MLA_FA_ERR_HIP;

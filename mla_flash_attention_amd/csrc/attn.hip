@@ -206,14 +206,8 @@ __device__ __forceinline__ void ragged_find(const RaggedPlan &p, int k, int &row
     }
 }
 
-// The plan's row table: one int32 per row, its first slot | its piece count << 16 (both
-// at most kRaggedRows), in the workspace's tail after the partials.  The first workgroup
-// of the attention launch writes it and the merge reads it.  Offset in floats from the
-// workspace base.
-__device__ __forceinline__ int64_t ragged_table_off(int n_split, int rows, int heads) {
-    return (int64_t)n_split * rows * heads * (int64_t)(kPartialEntryBytes / sizeof(float));
-}
-
+// The plan's row table (ragged_table_off) lives in the workspace's tail after the
+// partials; the first workgroup of the attention launch writes it and the merges read it.
 __device__ __forceinline__ void ragged_write_table(const RaggedPlan &p, int32_t *tab, int rows) {
     const int lane = threadIdx.x & 63;
     int carry = 0;

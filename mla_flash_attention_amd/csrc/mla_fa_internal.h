@@ -85,6 +85,11 @@ constexpr size_t kRaggedTableBytes = kRaggedRows * sizeof(int32_t);
 inline size_t partial_bytes(int64_t rows, int heads, int splits) {
     return (size_t)splits * rows * heads * kPartialEntryBytes + kRaggedTableBytes;
 }
+// The row table's offset in floats from the partials' base: one int32 per row, its first
+// slot | its piece count << 16 (both at most kRaggedRows).
+__host__ __device__ inline int64_t ragged_table_off(int splits, int rows, int heads) {
+    return (int64_t)splits * rows * heads * (int64_t)(kPartialEntryBytes / sizeof(float));
+}
 
 // Per-head attention with separate K (192 wide) and V (128 wide), 16-bit types.
 struct MhaArgs {
@@ -128,6 +133,8 @@ struct MergeProjArgs {
     float *out;
     int64_t out_rs;                // elements
     int n_rows, n_head, n_split;
+    int ragged;                    // nonzero: the partials follow a length-proportional plan
+                                   //   (each row's slots from the row table)
 };
 
 hipError_t launch_attention(const AttnArgs &a, int kv_kind, int shape, hipStream_t stream);

@@ -263,6 +263,21 @@ __global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a)
     const float *wl = wm + (int64_t)S * RH;
     const f32x2v *wsc = reinterpret_cast<const f32x2v *>(wl + (int64_t)S * RH);
     const uint16_t *wo = reinterpret_cast<const uint16_t *>(wsc + (int64_t)S * RH);
+    // Row r of the block: the (slot, head) entry of its first split, the stride between
+    // its splits, and their number.  Under a length-proportional plan its splits are the
+    // slots the row table gives it (a row with none reads slot 0 and weighs it 0).
+    auto row_splits = [&](int r, int64_t &e0, int64_t &es, int &ns) __attribute__((always_inline)) {
+        if (a.ragged) {
+            const unsigned v = reinterpret_cast<const unsigned *>(a.ws + ragged_table_off(S, a.n_rows, a.n_head))[r0 + r];
+            ns = (int)(v >> 16);
+            e0 = (int64_t)(ns > 0 ? (int)(v & 0xFFFFu) : 0) * a.n_head + h;
+            es = a.n_head;
+        } else {
+            e0 = (int64_t)(r0 + r) * a.n_head + h;
+            es = RH;
+            ns = S;
+        }
+    };
 
     // W rows of this wave: n-block nb of the half, reduction half kh (8 steps of 32)
     const int nb = wave & 3, kh = wave >> 2;
@@ -275,19 +290,24 @@ __global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a)
     const int pair = tid & 255, sg = tid >> 8;
     const int pr = pair >> 6, oc = pair & 63;
     const bool prow = pr < nrow;
-    const u32x4 *op = reinterpret_cast<const u32x4 *>(wo + ((int64_t)(r0 + (prow ? pr : 0)) * a.n_head + h) * kDV) + oc;
-    const int64_t step8 = RH * kDV / 8;               // stride between splits, in octets
+    int64_t pe0, pes;
+    int ps;                                            // splits of row pr
+    row_splits(prow ? pr : 0, pe0, pes, ps);
+    const u32x4 *op = reinterpret_cast<const u32x4 *>(wo + pe0 * kDV) + oc;
+    const int64_t step8 = pes * kDV / 8;              // stride between splits, in octets
     u32x4 v0[kMPBatch];
 #pragma unroll
     for (int u = 0; u < kMPBatch; ++u) {
         const int i = sg + 2 * u;
-        v0[u] = op[(int64_t)(i < S ? i : 0) * step8];   // unconditional: no wait until used
+        v0[u] = op[(int64_t)(i < ps ? i : 0) * step8];   // unconditional: no wait until used
     }
 
     // (m, l, scales) of row fr, splits ft, ft + 128, ...: max, weights, normaliser
     const int fr = tid >> 7, ft = tid & 127;
     const bool frow = fr < nrow;
-    const int64_t rhf = (int64_t)(r0 + (frow ? fr : 0)) * a.n_head + h;
+    int64_t fe0, fes;
+    int fs;                                            // splits of row fr
+    row_splits(frow ? fr : 0, fe0, fes, fs);
     float mv[kMPPer], lv[kMPPer];
     f32x2v scv[kMPPer];
     float mloc = -INFINITY;
@@ -295,10 +315,10 @@ __global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a)
     for (int j = 0; j < kMPPer; ++j) {
         const int i = ft + 128 * j;
         mv[j] = -INFINITY;
-        if (frow && i < S) {
-            mv[j] = wm[i * RH + rhf];
-            lv[j] = wl[i * RH + rhf];
-            scv[j] = wsc[i * RH + rhf];
+        if (frow && i < fs) {
+            mv[j] = wm[fe0 + i * fes];
+            lv[j] = wl[fe0 + i * fes];
+            scv[j] = wsc[fe0 + i * fes];
             mloc = fmaxf(mloc, mv[j]);
         }
     }
@@ -310,7 +330,7 @@ __global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a)
 #pragma unroll
     for (int j = 0; j < kMPPer; ++j) {
         const int i = ft + 128 * j;
-        if (frow && i < S) {
+        if (frow && i < fs) {
             const float wgt = (mstar == -INFINITY || mv[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv[j] - mstar);
             if (wgt != 0.f) lloc += wgt * lv[j];
             fac_s[0][fr][i] = wgt != 0.f ? wgt * scv[j][0] : 0.f;
@@ -333,20 +353,20 @@ __global__ void __launch_bounds__(kMPThreads) merge_proj_kernel(MergeProjArgs a)
 #pragma unroll
     for (int u = 0; u < kMPBatch; ++u) {
         const int i = sg + 2 * u;
-        const float wgt = prow && i < S ? f_s[i] : 0.f;
+        const float wgt = prow && i < ps ? f_s[i] : 0.f;
         if (wgt != 0.f) {                              // unweighted splits may hold any bits
             a0 += wgt * lo4(v0[u]);
             a1 += wgt * hi4(v0[u]);
         }
     }
-    for (int i0 = sg + 2 * kMPBatch; i0 < S; i0 += 2 * kMPBatch) {
+    for (int i0 = sg + 2 * kMPBatch; i0 < ps; i0 += 2 * kMPBatch) {
         u32x4 v[kMPBatch];
         float wt[kMPBatch];
 #pragma unroll
         for (int u = 0; u < kMPBatch; ++u) {
             const int i = i0 + 2 * u;
-            wt[u] = prow && i < S ? f_s[i] : 0.f;
-            v[u] = op[(int64_t)(i < S ? i : 0) * step8];
+            wt[u] = prow && i < ps ? f_s[i] : 0.f;
+            v[u] = op[(int64_t)(i < ps ? i : 0) * step8];
         }
 #pragma unroll
         for (int u = 0; u < kMPBatch; ++u)

@@ -105,3 +105,16 @@ def test_workspace_redzones():
     assert_parity(got, oracle.attention_problem(p), "redzones")
     assert torch.all(obuf[:pad] == 12345.0) and torch.all(obuf[-pad:] == 12345.0)
     assert torch.all(wbuf[:pad] == 77) and torch.all(wbuf[-pad:] == 77)
+
+
+@pytest.mark.parametrize("lengths,n_tok", [([0, 0, 20000, 0, 1, 3], 1), ([9000, 3, 4500, 0, 12000, 700, 2, 6000], 2)])
+def test_absorbed_ragged(lengths, n_tok):
+    """The absorbed decode over rows of very different lengths: the split attention
+    follows the plan and the fused merge + output projection reads each row's slots
+    (rows of a 4-row block holding different piece counts, some none)."""
+    from tests.test_gpu_absorbed import ref_absorbed, run_absorbed
+    p = synth.make_absorbed_problem(n_seq=len(lengths), n_tok=n_tok, n_head=128, n_kv=20000, q_type=BF16,
+                                    kv_type=BF16, seed=68 + n_tok, causal=n_tok > 1)
+    p.kv_len = np.asarray(lengths, dtype=np.int32)
+    got = run_absorbed(p, n_split=0)
+    assert_parity(got, ref_absorbed(p), f"absorbed ragged n_tok={n_tok}")
