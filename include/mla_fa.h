@@ -87,8 +87,8 @@ const char *mla_fa_strerror(int status);
 
 /* Library version as major*10000 + minor*100 + patch (2.0.0: mla_fa_attend takes
  * per-token sparse index lists; 2.1.0: mla_fa_absorbed fuses the split merge with the
- * output projection, three launches per call; mla_fa_attend and mla_fa_absorbed split
- * rows of device-side lengths in proportion to those lengths). */
+ * output projection, three launches per call; mla_fa_attend, mla_fa_absorbed and the
+ * sparse mla_fa_decode split rows of device-side lengths in proportion to them). */
 int mla_fa_version(void);
 
 /*
@@ -129,7 +129,9 @@ size_t mla_fa_workspace_size(int n_rows, int n_head, int64_t n_kv, int kv_type, 
  *                  result is then unspecified, but no read leaves the cache).
  *   scale          finite fp32 softmax scale (e.g. 1/sqrt(192)).
  *   out            [n_seq][n_head][512] fp32.
- *   n_split        0 = automatic, else 1 .. 1024 KV splits.
+ *   n_split        0 = automatic, else 1 .. 1024 KV splits.  With kv_idx and more than
+ *                  one sequence, a split call shares its partial slots out by the lists'
+ *                  lengths, as mla_fa_attend describes.
  *   workspace      device buffer of at least mla_fa_workspace_size(n_seq, n_head,
  *                  n_kv, kv_type, n_split) bytes (may be NULL when that is 0).
  */
@@ -145,7 +147,10 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
  * partials in the workspace (for n_split == 1 it writes `out` directly and there is
  * nothing to merge).  mla_fa_merge_partials combines the partials of a previous
  * mla_fa_decode_partials call with the same n_rows (= n_seq), n_head, n_split and
- * workspace into `out`.  mla_fa_decode is exactly these two calls in order.
+ * workspace into `out`.  mla_fa_decode is exactly these two calls in order, except with
+ * kv_idx over several sequences: there it shares the slots out by the lists' lengths,
+ * while the two phases keep n_split pieces per row so that the merge needs only the
+ * sizes (the results differ by floating-point reassociation alone).
  */
 int mla_fa_decode_partials(const void *q, int q_type, const void *kv, int kv_type,
                            int64_t kv_row_stride, int64_t kv_seq_stride, int n_seq, int n_head,

@@ -416,6 +416,7 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
     Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
                              mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
                              n_split, workspace, workspace_bytes);
+    c.ragged_ok = n_seq > 1;       // index lists of several sequences: share slots by count
     int st = validate(c);
     if (st) return st;
     Plan p = make_plan(n_seq, n_head, n_kv, kv_type, n_split);
@@ -424,7 +425,8 @@ int mla_fa_decode(const void *q, int q_type, const void *kv, int kv_type, int64_
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_partials(c, p, s);
     if (st) return st;
-    return run_merge(n_seq, n_head, p.n_split, out, workspace, workspace_bytes, s);
+    const Ragged rg = ragged_for(c, p);
+    return run_merge(n_seq, n_head, p.n_split, out, workspace, workspace_bytes, s, nullptr, &rg);
 }
 
 int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,
@@ -435,6 +437,7 @@ int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type
     Common c = decode_common(q, q_type, kv, kv_type, kv_row_stride, kv_seq_stride, n_seq, n_head, n_kv,
                              mask, mask_seq_stride, kv_idx, kv_idx_count, idx_seq_stride, scale, out,
                              n_split, nullptr, 0);
+    c.ragged_ok = n_seq > 1;       // as mla_fa_decode
     int st = validate(c);
     if (st) return st;
     Plan p = make_plan(n_seq, n_head, n_kv, kv_type, n_split);
@@ -448,7 +451,8 @@ int mla_fa_decode_noalloc(const void *q, int q_type, const void *kv, int kv_type
     hipStream_t s = static_cast<hipStream_t>(stream);
     st = run_partials(c, p, s);
     if (st) return st;
-    return run_merge(n_seq, n_head, p.n_split, out, c.ws, c.ws_bytes, s);
+    const Ragged rg = ragged_for(c, p);
+    return run_merge(n_seq, n_head, p.n_split, out, c.ws, c.ws_bytes, s, nullptr, &rg);
 }
 
 int mla_fa_prefill(const void *q, int q_type, const void *kv, int kv_type, int64_t kv_row_stride,

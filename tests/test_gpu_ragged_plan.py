@@ -118,3 +118,42 @@ def test_absorbed_ragged(lengths, n_tok):
     p.kv_len = np.asarray(lengths, dtype=np.int32)
     got = run_absorbed(p, n_split=0)
     assert_parity(got, ref_absorbed(p), f"absorbed ragged n_tok={n_tok}")
+
+
+@pytest.mark.parametrize("kv_type", [BF16, Q8])
+def test_sparse_decode_uneven_lists(kv_type):
+    """mla_fa_decode over the index lists of several sequences shares its slots by the
+    lists' lengths; the two-phase calls (partials, then merge) keep n_split pieces per
+    row.  Lists of ~all, a few, none and half of the cells: both forms against the
+    oracle, and the plan's output against the two-phase one."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    p = synth.make_problem(kind="sparse", n_seq=4, n_head=128, n_kv=12000, q_type=BF16, kv_type=kv_type, seed=69)
+    g = np.random.default_rng(69)
+    keep = [g.random(p.n_kv) < f for f in (0.98, 0.004, 0.0, 0.5)]
+    for s, k in enumerate(keep):
+        p.mask[s, 0] = np.where(k, np.uint16(0), np.uint16(synth.F16_NEG_INF))
+    mask = to_dev(p.mask.reshape(p.n_seq, p.n_kv))
+    idx = torch.zeros((p.n_seq, p.n_kv), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((p.n_seq,), dtype=torch.int32, device="cuda")
+    B.fa_mask_compact(mask, idx, cnt)
+    q, kv = to_dev(p.q.reshape(p.n_seq, p.n_head, synth.DK)), to_dev(p.kv)
+    ns = B.mla_fa_auto_splits(p.n_seq, p.n_head, p.n_kv, p.kv_type)
+    assert ns > 1
+    ws = B.workspace_for(p.n_seq, p.n_head, p.n_kv, p.kv_type, ns)
+    outs = []
+    for two_phase in (False, True):
+        out = torch.full((p.n_seq, p.n_head, synth.DV), float("nan"), dtype=torch.float32, device="cuda")
+        kw = dict(mask=mask, kv_idx=idx, kv_idx_count=cnt, n_split=ns, workspace=ws)
+        if two_phase:
+            B.mla_fa_decode_partials(q, p.q_type, kv, p.kv_type, p.scale, out, **kw)
+            B.mla_fa_merge_partials(p.n_seq, p.n_head, ns, out, ws)
+        else:
+            B.mla_fa_decode(q, p.q_type, kv, p.kv_type, p.scale, out, **kw)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy().reshape(-1, synth.DV).astype(np.float64))
+    ref = oracle.attention_problem(p)
+    assert_parity(outs[0], ref, f"plan kv{kv_type}")
+    assert_parity(outs[1], ref, f"two-phase kv{kv_type}")
+    assert_parity(outs[0], outs[1], f"plan vs two-phase kv{kv_type}")
+    assert np.all(outs[0][2 * p.n_head:3 * p.n_head] == 0)      # the sequence with no kept cell
