@@ -391,10 +391,11 @@ def _time_absorbed(B, p, steps, warmup):
     out = torch.empty((p.n_seq, p.n_tok, p.n_head, 128), dtype=torch.float32, device="cuda")
     ns = B.mla_fa_auto_splits(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type)
     ws = B.absorbed_workspace_for(p.n_seq * p.n_tok, p.n_head, p.n_kv, p.kv_type, ns)
+    kv_len = None if p.kv_len is None else _dev(p.kv_len)
 
     def call():
-        B.mla_fa_absorbed(qn, qp, p.q_type, wk, wv, kv, p.kv_type, p.scale, out, causal=p.causal, n_split=ns,
-                          workspace=ws, stream=stream)
+        B.mla_fa_absorbed(qn, qp, p.q_type, wk, wv, kv, p.kv_type, p.scale, out, kv_len=kv_len, causal=p.causal,
+                          n_split=ns, workspace=ws, stream=stream)
 
     _warm(lambda i: call(), warmup)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -599,6 +600,17 @@ def main():
             cells = p.n_seq * p.n_kv
             nbytes = cells * 1152 + 2 * p.n_head * 512 * 128 * 2
             sec["n4_absorbed_decode_4x128h_32768"] = dict(
+                ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3), n_split=r["n_split"],
+                algorithmic_bytes=nbytes, hbm_frac=nbytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            # the same projections over the ragged 2-token batch of the n3 lines (8 sequences
+            # of U{2..32768} valid cells, causal): the serving shape of absorbed decode
+            p = synth.make_absorbed_problem(8, 2, 128, 32768, synth.TYPE_BF16, synth.TYPE_BF16, seed=6, causal=True,
+                                            ragged=True)
+            r = _time_absorbed(B, p, args.steps, args.warmup)
+            lens = p.kv_len.astype(np.int64)
+            cells = int(sum(L - p.n_tok + t + 1 for L in lens for t in range(p.n_tok)))
+            nbytes = int(lens.sum()) * 1152 + 2 * p.n_head * 512 * 128 * 2
+            sec["n4_absorbed_ragged_2tok_8x128h"] = dict(
                 ms=r["step_ms"], cells_per_s=cells / (r["step_ms"] * 1e-3), n_split=r["n_split"],
                 algorithmic_bytes=nbytes, hbm_frac=nbytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
         if want("c4"):
