@@ -95,7 +95,9 @@ int mla_fa_version(void);
  * Number of KV splits the library picks when a call passes n_split = 0, for a call
  * with n_rows = n_seq * n_tok query rows.  Split-KV: each split attends to one range
  * of keys and leaves a partial (m, l, O); the partials are merged with the same
- * rescale-by-new-max rule the online softmax applies between tiles.
+ * rescale-by-new-max rule the online softmax applies between tiles.  The automatic plan
+ * fills the current device's compute units (256 on an MI355X, and 256 when no device is
+ * visible), so size a workspace with the device the call will run on current.
  */
 int mla_fa_auto_splits(int n_rows, int n_head, int64_t n_kv, int kv_type);
 

@@ -2,6 +2,7 @@
 // call), split planning, workspace layout and launches.  See include/mla_fa.h for the
 // contract of every entry point.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -14,8 +15,32 @@ using namespace mlafa;
 
 namespace {
 
-constexpr int kCUs = 256;                    // MI355X compute units (one workgroup each)
 constexpr int kMinTilesPerSplit = 1;   // short caches: one tile per split is fastest (latency-bound)
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device.  The plans give each CU one workgroup (the
+// attention kernels' LDS use allows no more), so a partitioned GPU, with fewer CUs per
+// device, gets plans of its own size.  256, the MI355X's count, when HIP cannot say (no
+// device), so that the host-only sizing calls still answer; a failed query's error is
+// cleared so that no later launch check reports it.  Cached per device.
+constexpr int kDefaultCUs = 256;
+int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];          // 0 = not asked yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+            (void)hipGetLastError();
+            n = kDefaultCUs;
+        }
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -101,18 +126,19 @@ int pick_shape(int n_head, int n_split, int kv_type) {
 int auto_splits(int64_t n_rows, int n_head, int64_t n_kv, int kv_type) {
     const int env = env_splits();
     if (env) return env;
+    const int cus = device_cus();
     const int hu = shape_heads(pick_shape(n_head, 1, kv_type));
-    if (n_rows * ((n_head + hu - 1) / hu) >= kCUs) return 1;
+    if (n_rows * ((n_head + hu - 1) / hu) >= cus) return 1;
     // splits that fill the chip with the split shape: the wide Q8_0 shape when that plan
     // stays within its split limit, else the 16-bit one
     int hs = shape_heads(pick_shape(n_head, 2, kv_type));
-    int64_t s = (kCUs + n_rows * ((n_head + hs - 1) / hs) - 1) / (n_rows * ((n_head + hs - 1) / hs));
+    int64_t s = (cus + n_rows * ((n_head + hs - 1) / hs) - 1) / (n_rows * ((n_head + hs - 1) / hs));
     // (the wide shape also needs the rounded-up plan to stay near one workgroup per CU)
     if (shape_heads(pick_shape(n_head, (int)(s < kMaxSplits ? s : kMaxSplits), kv_type)) != hs ||
-        n_rows * s * ((n_head + hs - 1) / hs) > kCUs + kCUs / 4) {
+        n_rows * s * ((n_head + hs - 1) / hs) > cus + cus / 4) {
         hs = shape_heads(pick_shape(n_head, kMaxSplits, kv_type));
         const int64_t hg = (n_head + hs - 1) / hs;
-        s = (kCUs + n_rows * hg - 1) / (n_rows * hg);
+        s = (cus + n_rows * hg - 1) / (n_rows * hg);
     }
     const int64_t max_by_len = (n_kv + kTileKeys * kMinTilesPerSplit - 1) / (kTileKeys * kMinTilesPerSplit);
     if (s > max_by_len) s = max_by_len;
@@ -209,7 +235,7 @@ int validate(const Common &c) {
 // Rows whose lengths only the device holds (valid lengths or index-list counts) get a
 // length-proportional plan when the call splits and runs its own merge: the kernel shares
 // the call's rows * n_split partial slots out by length, at most one piece per workgroup
-// slot of the chip (kCUs / head groups pieces, at least one per row).  With every row cut
+// slot of the chip (CUs / head groups pieces, at least one per row).  With every row cut
 // into n_split pieces instead, the longest row's pieces set the call's time.
 Ragged ragged_for(const Common &c, const Plan &p) {
     Ragged g;
@@ -217,7 +243,7 @@ Ragged ragged_for(const Common &c, const Plan &p) {
     const int64_t rows = (int64_t)c.n_seq * c.n_tok;
     if (!c.ragged_ok || p.n_split <= 1 || rows > kRaggedRows || (!c.kv_len && !c.kv_idx)) return g;
     const int64_t slots = rows * p.n_split;
-    const int64_t chip = std::max<int64_t>(rows, kCUs / p.head_groups);
+    const int64_t chip = std::max<int64_t>(rows, device_cus() / p.head_groups);
     g.budget = (int)std::min(slots, chip);
     g.kv_len = c.kv_idx ? nullptr : c.kv_len;
     g.count = c.kv_idx ? c.kv_idx_count : nullptr;
@@ -335,7 +361,6 @@ constexpr size_t kScratchBytes = MLA_FA_NOALLOC_SCRATCH_BYTES;
 static_assert(kScratchBytes % 256 == 0, "scratch size");
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices];
 

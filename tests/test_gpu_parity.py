@@ -31,6 +31,15 @@ def _decode_case(n_seq, n_head, n_kv, q_type, kv_type, seed, n_split=0, mask_kin
 
 
 # ---------------------------------------------------------------- workloads at full size
+def test_plan_fills_the_devices_compute_units():
+    """The automatic split plan sizes itself to the device's compute units: on the
+    4 x 128-head decode (two 64-head workgroups per key range) one workgroup per CU."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B.mla_fa_auto_splits(4, 128, 32768, BF16) == -(-cus // 8)
+
+
 def test_c1_full():
     p = synth.make_config(1)
     for n_split in (0, 1):
