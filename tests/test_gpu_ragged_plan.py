@@ -157,3 +157,57 @@ def test_sparse_decode_uneven_lists(kv_type):
     assert_parity(outs[1], ref, f"two-phase kv{kv_type}")
     assert_parity(outs[0], outs[1], f"plan vs two-phase kv{kv_type}")
     assert np.all(outs[0][2 * p.n_head:3 * p.n_head] == 0)      # the sequence with no kept cell
+
+
+def _expected_table(tiles, budget):
+    """The plan as documented: the smallest chunk C (in tiles) with
+    sum_r ceil(tiles_r / C) <= budget; row r gets ceil(tiles_r / C) pieces, numbered row
+    by row.  Returns [(first slot, pieces)] per row."""
+    C = 1
+    while sum(-(-t // C) for t in tiles) > budget:
+        C += 1
+    out, first = [], 0
+    for t in tiles:
+        n = -(-t // C)
+        out.append((first if n else 0, n))
+        first += n
+    return out
+
+
+@pytest.mark.parametrize("lengths,n_tok", [([11112, 6450, 7284, 19326, 11379, 21065, 9351, 25407], 2),
+                                           ([0, 5000, 1, 64, 65, 0, 30000], 1),
+                                           ([3000] * 20, 3)])
+def test_row_table_is_the_smallest_chunk_plan(lengths, n_tok):
+    """The row table the attention launch leaves in the workspace tail matches the plan
+    stated in plain terms: per row its first slot and piece count for the smallest
+    chunk that fits the budget (rows x n_split slots, at most one piece per workgroup
+    the chip holds: CUs / 2 head groups of 64 heads)."""
+    import torch
+    from mla_flash_attention_amd import binding as B
+    n_seq, n_head, n_kv = len(lengths), 128, 32768
+    p = synth.make_problem(kind="decode", n_seq=n_seq, n_tok=n_tok, n_head=n_head, n_kv=n_kv, seed=70,
+                           causal=n_tok > 1)
+    p.kv_len = np.asarray(lengths, dtype=np.int32)
+    rows = n_seq * n_tok
+    ns = B.mla_fa_auto_splits(rows, n_head, n_kv, p.kv_type)
+    ws = B.workspace_for(rows, n_head, n_kv, p.kv_type, ns)
+    ws.fill_(0x77)
+    out = torch.empty((n_seq, n_tok, n_head, synth.DV), dtype=torch.float32, device="cuda")
+    B.mla_fa_attend(to_dev(p.q), p.q_type, to_dev(p.kv), p.kv_type, p.scale, out,
+                    kv_len=torch.from_numpy(p.kv_len).cuda(), causal=n_tok > 1, n_split=ns, workspace=ws)
+    torch.cuda.synchronize()
+    tail = ns * rows * n_head * 1040
+    table = ws[tail:tail + 4 * rows].cpu().numpy().view(np.int32)
+    got = [(int(v) & 0xFFFF, int(v) >> 16) for v in table]
+    got = [(f if n else 0, n) for f, n in got]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    budget = min(rows * ns, max(rows, cus // 2))
+    tiles = []
+    for L in lengths:
+        for t in range(n_tok):
+            end = max(0, L - n_tok + t + 1) if n_tok > 1 else L
+            tiles.append(-(-end // 64))
+    assert got == _expected_table(tiles, budget)
+    assert sum(n for _, n in got) <= budget
+    assert_parity(out.cpu().numpy().reshape(-1, synth.DV).astype(np.float64), oracle.attention_problem(p),
+                  f"table case {lengths[:3]}")
