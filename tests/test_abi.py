@@ -311,3 +311,21 @@ def test_absorbed_launch_failures(L, monkeypatch, k, n_split):
     projection (fused with the merge of a split plan)."""
     monkeypatch.setenv("MLA_FA_FAIL_LAUNCH", str(k))
     assert _absorbed(L, n_split=n_split) == (B.MLA_FA_ERR_HIP if k <= 3 else B.MLA_FA_OK)
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/mla_fa.h needs no HIP header and compiles as strict C99 and as C++ (the
+    boundary takes plain pointers, sizes and a void * stream)."""
+    import shutil
+    import subprocess
+    inc = os.path.join(ROOT, "include")
+    src = tmp_path / "use.c"
+    src.write_text('#include "mla_fa.h"\nint main(void) { return mla_fa_version() > 0 ? 0 : 1; }\n')
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++11")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        args = [cc, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only", "-I", inc]
+        if cc == "g++":
+            args += ["-x", "c++"]
+        r = subprocess.run(args + [str(src)], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 0, r.stderr
